@@ -1,0 +1,146 @@
+"""Python binding of libattnres.so (argument marshalling only).
+
+The three entry points carry the names of the C ABI in ``include/attnres.h``
+and take torch tensors that live on the GPU: bfloat16 (or 16-bit integer
+views of bfloat16 bits) with contiguous rows. Every step of the computation
+runs in the library's HIP kernels; this module only reads pointers, strides
+and the current stream, calls the C function and raises ``AttnResError`` on a
+non-zero return code. There is no fallback: without the built library the
+import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import _build
+
+LIB_PATH = _build.LIB
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "(hipcc --offload-arch=gfx950)"
+    )
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P, _I64, _I, _F, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_lib.attnres_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I, _P, _P, _P, _P, _I64, _P,
+                             _I64, _F, _F, _I, _I, _I, _I, _I, _I, _P]
+_lib.wsgemm_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I, _I, _I, _P]
+_lib.attnres_oproj_workspace_size.argtypes = [_I, _I, _I]
+_lib.attnres_oproj_workspace_size.restype = _SZ
+_lib.attnres_oproj_run.argtypes = [_P, _I64, _P, _I64, _I, _P, _I64, _P, _I64, _I64, _I, _P, _P,
+                                   _P, _P, _I64, _P, _I64, _F, _F, _I, _I, _I, _I, _I, _I, _P,
+                                   _SZ, _P]
+_lib.attnres_strerror.argtypes = [_I]
+_lib.attnres_strerror.restype = ctypes.c_char_p
+for _f in (_lib.attnres_run, _lib.wsgemm_run, _lib.attnres_oproj_run):
+    _f.restype = _I
+
+EXPORTS = ("attnres_run", "wsgemm_run", "attnres_oproj_run", "attnres_oproj_workspace_size",
+           "attnres_strerror")
+
+
+class AttnResError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+
+
+def attnres_strerror(code: int) -> str:
+    return _lib.attnres_strerror(int(code)).decode()
+
+
+strerror = attnres_strerror
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise AttnResError(-1, "tensors must be on the GPU")
+    if t.element_size() != 2:
+        raise AttnResError(-1, "tensors must hold 16-bit (bfloat16) elements")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _row_stride(t):
+    if t is None:
+        return 0
+    if t.stride(-1) != 1:
+        raise AttnResError(-1, "rows must be contiguous")
+    return t.stride(-2) if t.dim() >= 2 else t.shape[-1]
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise AttnResError(rc, where)
+
+
+def wsgemm_run(x, W, y, stream=None):
+    """y[M, N] = bf16(x[M, K] W[N, K]^T) (-0.0 stored as +0.0)."""
+    M, K = x.shape
+    N = W.shape[0]
+    rc = _lib.wsgemm_run(_ptr(x), _row_stride(x), _ptr(W), _row_stride(W), _ptr(y),
+                         _row_stride(y), M, N, K, _stream(stream))
+    _check(rc, "wsgemm_run")
+    return y
+
+
+def attnres_run(delta, prefix, blocks, norm, query, out_norm, out, aux=None, *, nb, write=-1,
+                has_delta=1, final_boundary=0, eps=1e-6, out_eps=1e-6, stream=None):
+    """AttnRes of T = delta.shape[0] tokens; blocks [T, cap, H] (any token / slot strides)."""
+    T, H = delta.shape
+    if blocks is None:
+        bst_t = bst_b = cap = 0
+    else:
+        if blocks.stride(-1) != 1:
+            raise AttnResError(-1, "block rows must be contiguous")
+        bst_t, bst_b, cap = blocks.stride(0), blocks.stride(1), blocks.shape[1]
+    rc = _lib.attnres_run(_ptr(delta), _row_stride(delta), _ptr(prefix), _row_stride(prefix),
+                          _ptr(blocks), bst_t, bst_b, cap, _ptr(norm), _ptr(query),
+                          _ptr(out_norm), _ptr(out), _row_stride(out), _ptr(aux),
+                          _row_stride(aux), eps, out_eps, T, H, nb, write, int(has_delta),
+                          int(final_boundary), _stream(stream))
+    _check(rc, "attnres_run")
+    return out, prefix, blocks
+
+
+def attnres_oproj_workspace_size(M: int, H: int, nb: int) -> int:
+    return int(_lib.attnres_oproj_workspace_size(M, H, nb))
+
+
+def make_workspace(M: int, H: int, nb: int, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace for attnres_oproj_run (torch allocates it)."""
+    return torch.zeros(attnres_oproj_workspace_size(M, H, nb), dtype=torch.uint8, device=device)
+
+
+def attnres_oproj_run(x, W, prefix, blocks, norm, query, out_norm, out, aux, workspace, *, nb,
+                      write=-1, has_delta=1, final_boundary=0, eps=1e-6, out_eps=1e-6,
+                      stream=None):
+    """Fused o-projection + AttnRes: delta = bf16(x W^T), then AttnRes (T = M)."""
+    M, K = x.shape
+    H = W.shape[0]
+    if blocks is None:
+        bst_t = bst_b = cap = 0
+    else:
+        if blocks.stride(-1) != 1:
+            raise AttnResError(-1, "block rows must be contiguous")
+        bst_t, bst_b, cap = blocks.stride(0), blocks.stride(1), blocks.shape[1]
+    ws = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.attnres_oproj_run(_ptr(x), _row_stride(x), _ptr(W), _row_stride(W), K, _ptr(prefix),
+                                _row_stride(prefix), _ptr(blocks), bst_t, bst_b, cap, _ptr(norm),
+                                _ptr(query), _ptr(out_norm), _ptr(out), _row_stride(out),
+                                _ptr(aux), _row_stride(aux), eps, out_eps, M, H, nb, write,
+                                int(has_delta), int(final_boundary), ws, wsb, _stream(stream))
+    _check(rc, "attnres_oproj_run")
+    return out, prefix, blocks

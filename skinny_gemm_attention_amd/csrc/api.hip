@@ -1,0 +1,183 @@
+// C ABI of the decode-step hot path (declared in include/attnres.h).
+//
+// Every argument is checked here, on the host, before any HIP call: an invalid
+// call returns a negative code and enqueues nothing.
+#include "../../include/attnres.h"
+#include "launch.hpp"
+
+namespace {
+
+using attnres::AttnParams;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool stride8(int64_t s) { return s >= 0 && (s & 7) == 0; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? ATTNRES_OK : ATTNRES_EHIP; }
+
+// Checks shared by attnres_run and attnres_oproj_run (T tokens).
+int check_attnres(const void* prefix, int64_t ld_prefix, const void* blocks, int64_t bst_t,
+                  int64_t bst_b, int cap, const void* norm, const void* query,
+                  const void* out_norm, const void* out, int64_t ld_out, const void* aux,
+                  int64_t ld_aux, float eps, float out_eps, int T, int H, int nb, int write,
+                  int has_delta, int final_boundary) {
+  if (T < 0 || H < 0 || cap < 0) return ATTNRES_EINVAL;
+  if ((has_delta != 0 && has_delta != 1) || (final_boundary != 0 && final_boundary != 1))
+    return ATTNRES_EINVAL;
+  if (!prefix || !norm || !query || !out_norm || !out) return ATTNRES_EINVAL;
+  if (!(eps >= 0.0f) || !(out_eps >= 0.0f) || eps > 1e30f || out_eps > 1e30f) return ATTNRES_EINVAL;
+  if (H < 8 || H > ATTNRES_MAX_H || (H & 7)) return ATTNRES_EUNSUPPORTED;
+  if (nb < 0 || nb > ATTNRES_MAX_BLOCKS || nb > cap) return ATTNRES_ERANGE;
+  if (write < -1 || write >= cap) return ATTNRES_ERANGE;
+  const bool uses_blocks = nb > 0 || write >= 0;
+  if (uses_blocks && !blocks) return ATTNRES_EINVAL;
+  if (ld_prefix < H || ld_out < H || (aux && ld_aux < H)) return ATTNRES_EINVAL;
+  if (!aligned16(prefix) || !aligned16(norm) || !aligned16(query) || !aligned16(out_norm) ||
+      !aligned16(out) || (aux && !aligned16(aux)) || (uses_blocks && !aligned16(blocks)))
+    return ATTNRES_EALIGN;
+  if (!stride8(ld_prefix) || !stride8(ld_out) || (aux && !stride8(ld_aux))) return ATTNRES_EALIGN;
+  if (uses_blocks) {
+    if (bst_t < H || bst_b < H) return ATTNRES_EINVAL;
+    if (!stride8(bst_t) || !stride8(bst_b)) return ATTNRES_EALIGN;
+    const bool token_major = bst_t >= (int64_t)cap * bst_b;
+    const bool slot_major = bst_b >= (int64_t)T * bst_t;
+    if (!token_major && !slot_major) return ATTNRES_EINVAL;  // rows would overlap
+  }
+  return ATTNRES_OK;
+}
+
+AttnParams make_params(const void* delta, int64_t ld_delta, void* prefix, int64_t ld_prefix,
+                       void* blocks, int64_t bst_t, int64_t bst_b, const void* norm,
+                       const void* query, const void* out_norm, void* out, int64_t ld_out,
+                       void* aux, int64_t ld_aux, float eps, float out_eps, int T, int H, int nb,
+                       int write, int has_delta, int final_boundary) {
+  AttnParams p;
+  p.delta = static_cast<const uint16_t*>(delta);
+  p.ld_delta = ld_delta;
+  p.prefix = static_cast<uint16_t*>(prefix);
+  p.ld_prefix = ld_prefix;
+  p.blocks = static_cast<uint16_t*>(blocks);
+  p.bst_t = bst_t;
+  p.bst_b = bst_b;
+  p.norm = static_cast<const uint16_t*>(norm);
+  p.query = static_cast<const uint16_t*>(query);
+  p.out_norm = static_cast<const uint16_t*>(out_norm);
+  p.out = static_cast<uint16_t*>(out);
+  p.ld_out = ld_out;
+  p.aux = static_cast<uint16_t*>(aux);
+  p.ld_aux = ld_aux;
+  p.eps = eps;
+  p.out_eps = out_eps;
+  p.inv_h = 1.0f / (float)H;
+  p.T = T;
+  p.H = H;
+  p.nb = nb;
+  p.write = write;
+  p.has_delta = has_delta;
+  p.final_b = final_boundary;
+  return p;
+}
+
+constexpr size_t kWorkspaceBytes = 256;
+
+}  // namespace
+
+extern "C" {
+
+int attnres_run(const void* delta, int64_t ld_delta, void* prefix, int64_t ld_prefix,
+                void* blocks, int64_t blk_stride_t, int64_t blk_stride_b, int cap,
+                const void* norm, const void* query, const void* out_norm, void* out,
+                int64_t ld_out, void* aux, int64_t ld_aux, float eps, float out_eps, int T,
+                int H, int nb, int write, int has_delta, int final_boundary, void* stream) {
+  if (T < 0) return ATTNRES_EINVAL;
+  if (T == 0) return ATTNRES_OK;  // nothing to read or write
+  int rc = check_attnres(prefix, ld_prefix, blocks, blk_stride_t, blk_stride_b, cap, norm, query,
+                         out_norm, out, ld_out, aux, ld_aux, eps, out_eps, T, H, nb, write,
+                         has_delta, final_boundary);
+  if (rc) return rc;
+  if (!delta) return ATTNRES_EINVAL;
+  if (ld_delta < H) return ATTNRES_EINVAL;
+  if (!aligned16(delta)) return ATTNRES_EALIGN;
+  if (!stride8(ld_delta)) return ATTNRES_EALIGN;
+  AttnParams p = make_params(delta, ld_delta, prefix, ld_prefix, blocks, blk_stride_t,
+                             blk_stride_b, norm, query, out_norm, out, ld_out, aux, ld_aux, eps,
+                             out_eps, T, H, nb, write, has_delta, final_boundary);
+  return from_hip(attnres::launch_attnres(p, static_cast<hipStream_t>(stream)));
+}
+
+int wsgemm_run(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, int64_t ldy,
+               int M, int N, int K, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return ATTNRES_EINVAL;
+  if (M == 0) return ATTNRES_OK;  // nothing to read or write
+  if (!y || (K > 0 && (!x || !W))) return ATTNRES_EINVAL;  // x, W unread when K == 0
+  if (M > ATTNRES_MAX_M) return ATTNRES_ERANGE;
+  if (N < 8 || (N & 7) || (K & 7)) return ATTNRES_EUNSUPPORTED;
+  if (ldy < N || (K > 0 && (ldx < K || ldw < K))) return ATTNRES_EINVAL;
+  if (!aligned16(y) || (K > 0 && (!aligned16(x) || !aligned16(W)))) return ATTNRES_EALIGN;
+  if (!stride8(ldy) || (K > 0 && (!stride8(ldx) || !stride8(ldw)))) return ATTNRES_EALIGN;
+  attnres::GemmParams p;
+  p.x = static_cast<const uint16_t*>(x);
+  p.ldx = ldx;
+  p.W = static_cast<const uint16_t*>(W);
+  p.ldw = ldw;
+  p.y = static_cast<uint16_t*>(y);
+  p.ldy = ldy;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  return from_hip(attnres::launch_wsgemm(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t attnres_oproj_workspace_size(int M, int H, int nb) {
+  (void)M;
+  (void)H;
+  (void)nb;
+  return kWorkspaceBytes;
+}
+
+int attnres_oproj_run(const void* x, int64_t ldx, const void* W, int64_t ldw, int K, void* prefix,
+                      int64_t ld_prefix, void* blocks, int64_t blk_stride_t,
+                      int64_t blk_stride_b, int cap, const void* norm, const void* query,
+                      const void* out_norm, void* out, int64_t ld_out, void* aux, int64_t ld_aux,
+                      float eps, float out_eps, int M, int H, int nb, int write, int has_delta,
+                      int final_boundary, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int rc = check_attnres(prefix, ld_prefix, blocks, blk_stride_t, blk_stride_b, cap, norm, query,
+                         out_norm, out, ld_out, aux, ld_aux, eps, out_eps, M, H, nb, write,
+                         has_delta, final_boundary);
+  if (rc) return rc;
+  if (K < 0 || (K > 0 && (!x || !W))) return ATTNRES_EINVAL;  // x, W unread when K == 0
+  if (M < 1 || M > ATTNRES_MAX_M) return ATTNRES_ERANGE;
+  if (K & 7) return ATTNRES_EUNSUPPORTED;
+  if (K > 0 && (ldx < K || ldw < K)) return ATTNRES_EINVAL;
+  if (K > 0 && (!aligned16(x) || !aligned16(W))) return ATTNRES_EALIGN;
+  if (K > 0 && (!stride8(ldx) || !stride8(ldw))) return ATTNRES_EALIGN;
+  if (!workspace || workspace_bytes < kWorkspaceBytes ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return ATTNRES_EWORKSPACE;
+  attnres::FusedParams p;
+  p.a = make_params(nullptr, 0, prefix, ld_prefix, blocks, blk_stride_t, blk_stride_b, norm, query,
+                    out_norm, out, ld_out, aux, ld_aux, eps, out_eps, M, H, nb, write, has_delta,
+                    final_boundary);
+  p.x = static_cast<const uint16_t*>(x);
+  p.ldx = ldx;
+  p.W = static_cast<const uint16_t*>(W);
+  p.ldw = ldw;
+  p.K = K;
+  p.sync = static_cast<attnres::FusedSync*>(workspace);
+  return from_hip(attnres::launch_fused(p, static_cast<hipStream_t>(stream)));
+}
+
+const char* attnres_strerror(int code) {
+  switch (code) {
+    case ATTNRES_OK: return "success";
+    case ATTNRES_EINVAL: return "invalid argument (null pointer, size or stride)";
+    case ATTNRES_EALIGN: return "pointer not 16-byte aligned or stride not a multiple of 8 elements";
+    case ATTNRES_ERANGE: return "nb, write, cap, M or T out of range";
+    case ATTNRES_EUNSUPPORTED: return "shape not supported (H, N or K limits)";
+    case ATTNRES_EWORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case ATTNRES_EHIP: return "HIP launch failed";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

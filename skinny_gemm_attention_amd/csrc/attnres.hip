@@ -1,0 +1,99 @@
+// AttnRes with the delta given as a tensor (vLLM attn_res.kernel page,
+// ClusterAttnRes with a tensor delta): one workgroup per token.
+//
+// Every load of the token is issued up front (saved blocks, norm, query,
+// out_norm, delta, old prefix), so one DRAM round trip covers the whole row
+// set; the two (final boundary: three) 7168-wide sums are fixed-order
+// workgroup reductions.
+#include "launch.hpp"
+
+namespace attnres {
+
+template <int NT>
+__global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
+  constexpr int NW = TokenShape<NT>::NW, NCH = TokenShape<NT>::NCH;
+  __shared__ float lds_pre[NW * 16], lds_post[NW * 4], lds_fin[NW];
+  const int t = blockIdx.x, tid = threadIdx.x, CH = a.H >> 3;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  u32x4 vb[kMaxBlocks][NCH], g[NCH], d[NCH], p[NCH];
+  float w[NCH][8];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = tid + j * NT;
+    const bool valid = c < CH;
+    const size_t col = (size_t)c * 8;
+#pragma unroll
+    for (int b = 0; b < kMaxBlocks; ++b)
+      vb[b][j] = (valid && b < a.nb) ? ld16(a.blocks + t * a.bst_t + b * a.bst_b + col) : zero;
+    g[j] = valid ? ld16(a.out_norm + col) : zero;
+    d[j] = valid ? ld16(a.delta + t * a.ld_delta + col) : zero;
+    p[j] = (valid && a.has_delta) ? ld16(a.prefix + t * a.ld_prefix + col) : zero;
+    if (valid) {
+      weights8(a, c, w[j]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[j][i] = 0.0f;
+    }
+  }
+
+  // pre: saved-block statistics and the unnormalised mixture
+  float mix[NCH][8];
+  PreScalars pre = {0.0f, 0.0f};
+  if (a.nb > 0) {
+    float ps[16];
+    pre_partials(vb, w, a.nb, ps);
+    wg_sum<16, NW>(ps, lds_pre);
+    pre = pre_finish(ps, vb, a.nb, a.eps, a.inv_h, mix);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mix[j][i] = 0.0f;
+  }
+
+  // residual update: new = bf16(prefix + delta), or the delta itself
+  u32x4 nbits[NCH];
+  float nw[NCH][8];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    if (a.has_delta) {
+      float pf[8], df[8];
+      unpack8(p[j], pf);
+      unpack8(d[j], df);
+      nbits[j].x = pack2(add_round_odd(pf[0], df[0]), add_round_odd(pf[1], df[1]));
+      nbits[j].y = pack2(add_round_odd(pf[2], df[2]), add_round_odd(pf[3], df[3]));
+      nbits[j].z = pack2(add_round_odd(pf[4], df[4]), add_round_odd(pf[5], df[5]));
+      nbits[j].w = pack2(add_round_odd(pf[6], df[6]), add_round_odd(pf[7], df[7]));
+    } else {
+      nbits[j] = d[j];
+    }
+    unpack8(nbits[j], nw[j]);
+  }
+
+  float pp[4];
+  post_partials(nw, w, mix, pp);
+  wg_sum<4, NW>(pp, lds_post);
+
+  // state: the same bits go to prefix, aux and the written block slot
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = tid + j * NT;
+    if (c < CH) {
+      const size_t col = (size_t)c * 8;
+      st16(a.prefix + t * a.ld_prefix + col, nbits[j]);
+      if (a.aux) st16(a.aux + t * a.ld_aux + col, nbits[j]);
+      if (a.write >= 0) st16(a.blocks + t * a.bst_t + a.write * a.bst_b + col, nbits[j]);
+    }
+  }
+
+  finish_out<NT, NCH>(a, t, pre, pp, nw, mix, g, lds_fin);
+}
+
+hipError_t launch_attnres(const AttnParams& p, hipStream_t stream) {
+  constexpr int NT = 512;
+  hipLaunchKernelGGL((attnres_kernel<NT>), dim3(p.T), dim3(NT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace attnres

@@ -1,0 +1,144 @@
+// Device helpers for gfx950 (CDNA4, wave64): bfloat16 packing, exact
+// residual rounding, 16-byte loads, and fixed-order wavefront / workgroup
+// reductions built on DPP and LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnres {
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxBlocks = 8;   // saved blocks per token
+constexpr int kMaxH = 8192;     // widest AttnRes row
+constexpr int kMaxM = 64;       // tokens per GEMM call
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- bfloat16 <-> float ----------------------------------------------------
+
+// Low / high bfloat16 of a packed pair, widened exactly.
+__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ void unpack8(const u32x4 v, float (&f)[8]) {
+  f[0] = bf_lo(v.x); f[1] = bf_hi(v.x);
+  f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+  f[4] = bf_lo(v.z); f[5] = bf_hi(v.z);
+  f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+}
+
+// Round two floats to bfloat16 (nearest even; v_cvt_pk_bf16_f32), packed with
+// `a` in the low half.
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+  f32x2 p = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(p, bf16x2));
+}
+
+__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
+  u32x4 r;
+  r.x = pack2(f[0], f[1]);
+  r.y = pack2(f[2], f[3]);
+  r.z = pack2(f[4], f[5]);
+  r.w = pack2(f[6], f[7]);
+  return r;
+}
+
+// -0.0 halves of a bfloat16 pair become +0.0 (gemm.ws_gemm page, positive_zero).
+__device__ __forceinline__ unsigned positive_zero(unsigned w) {
+  if ((w & 0xFFFFu) == 0x8000u) w &= 0xFFFF0000u;
+  if ((w >> 16) == 0x8000u) w &= 0x0000FFFFu;
+  return w;
+}
+
+// a + b rounded to odd at float precision. With a and b bfloat16 values the
+// result, rounded once more to bfloat16 (nearest even), is the correctly
+// rounded bfloat16 sum: round-to-odd with 24 bits keeps enough information for
+// the 8-bit rounding that follows (a standard double-rounding-safe scheme).
+// TwoSum (Knuth) gives the exact error of the float sum.
+__device__ __forceinline__ float add_round_odd(float a, float b) {
+  const float s = a + b;
+  const float bb = s - a;
+  const float err = (a - (s - bb)) + (b - bb);
+  unsigned u = __float_as_uint(s);
+  if (err != 0.0f && (u & 1u) == 0u) {
+    const bool away = (err > 0.0f) == (s > 0.0f);  // true value lies farther from zero
+    u = away ? u + 1u : u - 1u;
+  }
+  return __uint_as_float(u);
+}
+
+// Reciprocal RMS of a row from its sum of squares (attn_res.kernel page,
+// helper rstd): rsqrt(sum_sq / H + eps), v_rsq_f32.
+__device__ __forceinline__ float rstd(float sum_sq, float inv_h, float eps) {
+  return __builtin_amdgcn_rsqf(__builtin_fmaf(sum_sq, inv_h, eps));
+}
+
+// e^x through v_exp_f32 (2^x).
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+// ---- memory -----------------------------------------------------------------
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Streamed-once data (the weight matrix): non-temporal hint.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// ---- fixed-order reductions --------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Sum over the 64 lanes of a wavefront, in a fixed tree: butterflies inside
+// each 16-lane row (xor 1, xor 2, half-row mirror, row mirror; the two addends
+// of every pair are the same numbers, so all lanes of a row agree bit for bit),
+// then ((row0 + row1) + (row2 + row3)). Must be called with all lanes active.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
+}
+
+// Sums K per-thread partials over a workgroup of NW wavefronts: wavefront sums
+// (wave_sum), then the NW wavefront totals in wavefront order. Every thread
+// gets the totals in v. `lds` holds NW*K floats and must not be reused by
+// another reduction of the same workgroup until all threads have returned.
+// Contains a workgroup barrier: call from uniform control flow.
+template <int K, int NW>
+__device__ __forceinline__ void wg_sum(float (&v)[K], float* lds) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float t[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) t[k] = wave_sum(v[k]);
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) lds[wave * K + k] = t[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    float s = lds[k];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) s += lds[w * K + k];
+    v[k] = s;
+  }
+}
+
+}  // namespace attnres

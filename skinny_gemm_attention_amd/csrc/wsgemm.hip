@@ -1,0 +1,57 @@
+// Standalone weight-stationary skinny GEMM (vLLM gemm.ws_gemm page, WsGemm):
+// y = bf16(x W^T) with -0.0 stored as +0.0 (positive_zero).
+#include "gemm.hpp"
+#include "launch.hpp"
+
+namespace attnres {
+
+template <int RT, int TT, int NW, int D>
+__global__ __launch_bounds__(NW * 64) void wsgemm_kernel(GemmParams p, int R) {
+  using C = GemmCore<RT, TT, NW, D>;
+  __shared__ f32x4 red[NW * C::kQuads];
+  const int row0 = blockIdx.x * R;
+  const int rows = min(R, p.N - row0);
+  f32x4 acc[RT][TT];
+  C::accumulate(p.x, p.ldx, p.W, p.ldw, p.M, p.K, row0, rows, acc);
+  C::stash(red, acc);
+  __syncthreads();
+  for (int q = threadIdx.x; q < C::kQuads; q += C::NT) {
+    int m, r;
+    C::quad_coords(q, m, r);
+    if (m < p.M && r < rows) {
+      const f32x4 s = C::gather(red, q);
+      const u32x2 v = {positive_zero(pack2(s.x, s.y)), positive_zero(pack2(s.z, s.w))};
+      st8(p.y + (size_t)m * p.ldy + row0 + r, v);
+    }
+  }
+}
+
+template <int RT, int TT>
+static hipError_t go(const GemmParams& p, int R, hipStream_t stream) {
+  constexpr int NW = 8;
+  constexpr int D = TT == 1 ? 8 : TT == 2 ? 6 : 4;
+  const int grid = (p.N + R - 1) / R;
+  hipLaunchKernelGGL((wsgemm_kernel<RT, TT, NW, D>), dim3(grid), dim3(NW * 64), 0, stream, p, R);
+  return hipGetLastError();
+}
+
+hipError_t launch_wsgemm(const GemmParams& p, hipStream_t stream) {
+  const int R = gemm_rows_per_wg(p.N);
+  const int tt = (p.M + 15) / 16;
+  if (R > 16) {
+    switch (tt) {
+      case 1: return go<2, 1>(p, R, stream);
+      case 2: return go<2, 2>(p, R, stream);
+      case 3: return go<2, 3>(p, R, stream);
+      default: return go<2, 4>(p, R, stream);
+    }
+  }
+  switch (tt) {
+    case 1: return go<1, 1>(p, R, stream);
+    case 2: return go<1, 2>(p, R, stream);
+    case 3: return go<1, 3>(p, R, stream);
+    default: return go<1, 4>(p, R, stream);
+  }
+}
+
+}  // namespace attnres

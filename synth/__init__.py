@@ -200,7 +200,7 @@ def decode_step(
     x = W = delta = None
     if K is not None:
         x = g("x", (M, K))
-        W = g("W", (H, K), 1.0 / math.sqrt(K))
+        W = g("W", (H, K), 1.0 / math.sqrt(max(K, 1)))
     if with_delta or K is None:
         delta = g("delta", (M, H))
     prefix = g("prefix", (M, H))

@@ -1,0 +1,140 @@
+"""The C-ABI library: it loads without a GPU, exports every entry point the
+header declares, and rejects invalid arguments on the host (no HIP call is
+made by any case here)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnres.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from skinny_gemm_attention_amd import _build
+
+    if _build.stale():
+        _build.build()
+    L = ctypes.CDLL(_build.LIB)
+    P, I64, I, F, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attnres_run.argtypes = [P, I64, P, I64, P, I64, I64, I, P, P, P, P, I64, P, I64, F, F, I, I,
+                              I, I, I, I, P]
+    L.wsgemm_run.argtypes = [P, I64, P, I64, P, I64, I, I, I, P]
+    L.attnres_oproj_run.argtypes = [P, I64, P, I64, I, P, I64, P, I64, I64, I, P, P, P, P, I64, P,
+                                    I64, F, F, I, I, I, I, I, I, P, SZ, P]
+    L.attnres_oproj_workspace_size.argtypes = [I, I, I]
+    L.attnres_oproj_workspace_size.restype = SZ
+    L.attnres_strerror.argtypes = [I]
+    L.attnres_strerror.restype = ctypes.c_char_p
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^(?:int|size_t|const char\*)\s+(\w+)\(", text, flags=re.M)
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert set(names) == {"attnres_run", "wsgemm_run", "attnres_oproj_workspace_size",
+                          "attnres_oproj_run", "attnres_strerror"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_names_match_header():
+    import skinny_gemm_attention_amd as sga
+
+    for n in declared_functions():
+        assert n in sga.EXPORTS and hasattr(sga, n), n
+
+
+def test_strerror_and_workspace(lib):
+    codes = {0: b"success", -1: b"invalid", -2: b"aligned", -3: b"range", -4: b"supported",
+             -5: b"workspace", -6: b"HIP"}
+    for c, word in codes.items():
+        assert word in lib.attnres_strerror(c)
+    assert b"unknown" in lib.attnres_strerror(-99)
+    assert lib.attnres_oproj_workspace_size(64, 7168, 8) >= 8
+
+
+# Fake, 256-byte-aligned addresses: validation only looks at their values.
+A = 0x10000
+H = 7168
+
+
+def attn_args(**kw):
+    a = dict(delta=A, ld_delta=H, prefix=A, ld_prefix=H, blocks=A, bst_t=9 * H, bst_b=H, cap=9,
+             norm=A, query=A, out_norm=A, out=A, ld_out=H, aux=A, ld_aux=H, eps=1e-6,
+             out_eps=1e-6, T=4, H=H, nb=8, write=8, has_delta=1, final=0, stream=None)
+    a.update(kw)
+    return a
+
+
+def call_attn(lib, a):
+    return lib.attnres_run(a["delta"], a["ld_delta"], a["prefix"], a["ld_prefix"], a["blocks"],
+                           a["bst_t"], a["bst_b"], a["cap"], a["norm"], a["query"],
+                           a["out_norm"], a["out"], a["ld_out"], a["aux"], a["ld_aux"], a["eps"],
+                           a["out_eps"], a["T"], a["H"], a["nb"], a["write"], a["has_delta"],
+                           a["final"], a["stream"])
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(delta=None), -1), (dict(prefix=None), -1), (dict(norm=None), -1), (dict(out=None), -1),
+    (dict(T=-1), -1), (dict(has_delta=2), -1), (dict(final=3), -1), (dict(eps=-1.0), -1),
+    (dict(eps=float("nan")), -1), (dict(ld_delta=H - 8), -1), (dict(ld_out=100), -1),
+    (dict(H=7160 + 4), -4), (dict(H=0), -4), (dict(H=8200), -4),
+    (dict(nb=9, cap=10, bst_t=10 * H), -3), (dict(nb=-1), -3), (dict(nb=8, cap=7, write=-1, bst_t=7 * H), -3),
+    (dict(write=9), -3), (dict(write=-2), -3),
+    (dict(blocks=None), -1), (dict(bst_b=H - 8), -1), (dict(bst_t=8 * H), -1),
+    (dict(delta=A + 8), -2), (dict(out=A + 2), -2), (dict(aux=A + 4), -2), (dict(blocks=A + 8), -2),
+    (dict(ld_out=H + 4), -2), (dict(bst_b=H + 4, bst_t=9 * H + 36), -2),
+])
+def test_attnres_run_rejects(lib, change, code):
+    assert call_attn(lib, attn_args(**change)) == code
+
+
+def test_attnres_run_empty_is_a_noop(lib):
+    assert call_attn(lib, attn_args(T=0)) == 0
+
+
+def call_gemm(lib, x=A, ldx=1024, W=A, ldw=1024, y=A, ldy=4096, M=8, N=4096, K=1024):
+    return lib.wsgemm_run(x, ldx, W, ldw, y, ldy, M, N, K, None)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(x=None), -1), (dict(W=None), -1), (dict(y=None), -1), (dict(M=-1), -1), (dict(K=-8), -1),
+    (dict(M=65), -3), (dict(N=4), -4), (dict(N=4100), -4), (dict(K=1020, ldx=1024), -4),
+    (dict(ldx=1016), -1), (dict(ldy=4088), -1), (dict(x=A + 8), -2), (dict(ldw=1028), -2),
+])
+def test_wsgemm_run_rejects(lib, change, code):
+    assert call_gemm(lib, **change) == code
+
+
+def test_wsgemm_run_empty_is_a_noop(lib):
+    assert call_gemm(lib, M=0) == 0
+
+
+def call_fused(lib, **kw):
+    a = attn_args()
+    a.update(x=A, ldx=8192, W=A, ldw=8192, K=8192, ws=A, wsb=256, M=4)
+    a.update(kw)
+    return lib.attnres_oproj_run(a["x"], a["ldx"], a["W"], a["ldw"], a["K"], a["prefix"],
+                                 a["ld_prefix"], a["blocks"], a["bst_t"], a["bst_b"], a["cap"],
+                                 a["norm"], a["query"], a["out_norm"], a["out"], a["ld_out"],
+                                 a["aux"], a["ld_aux"], a["eps"], a["out_eps"], a["M"], a["H"],
+                                 a["nb"], a["write"], a["has_delta"], a["final"], a["ws"],
+                                 a["wsb"], None)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(x=None), -1), (dict(W=None), -1), (dict(M=0), -3), (dict(M=65), -3), (dict(K=8190), -4),
+    (dict(ldx=4096), -1), (dict(W=A + 8), -2), (dict(ws=None), -5), (dict(wsb=8), -5),
+    (dict(ws=A + 16), -5), (dict(nb=9, cap=10, bst_t=10 * H), -3), (dict(H=100), -4),
+])
+def test_attnres_oproj_run_rejects(lib, change, code):
+    assert call_fused(lib, **change) == code

@@ -1,0 +1,136 @@
+"""Parity of attnres_oproj_run (the fused o-projection + AttnRes, HIP gfx950)
+with the FP64 oracle, on the three decode-step workloads and edge cases.
+
+The o-projection output is the AttnRes delta (vLLM oproj.prepared page),
+rounded to bf16 with -0.0 made +0.0 (gemm.ws_gemm page, positive_zero), so the
+fused call must equal wsgemm_run followed by attnres_run bit for bit. Against
+the oracle the FP32 accumulation of the GEMM may move a delta by one bf16 ulp,
+so out and the new prefix are held to the two-ulp / 5e-3 relative-L2 bound.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_tools import DEV, down, lib, up
+from parity_tools import assert_fused_out_close, assert_new_prefix_close, bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+POISON = 0x7FC1
+
+
+def fused(s, *, final, write=None, has_delta=None, aux=True, ws=None):
+    sga = lib()
+    write = s.write if write is None else write
+    has_delta = s.has_delta if has_delta is None else has_delta
+    prefix, blocks = up(s.prefix), up(s.blocks)
+    out = torch.full((s.M, s.H), POISON, dtype=torch.int16, device=DEV)
+    auxg = torch.full((s.M, s.H), POISON, dtype=torch.int16, device=DEV) if aux else None
+    ws = sga.make_workspace(s.M, s.H, s.nb, DEV) if ws is None else ws
+    sga.attnres_oproj_run(up(s.x), up(s.W), prefix, blocks, up(s.norm), up(s.query),
+                          up(s.out_norm), out, auxg, ws, nb=s.nb, write=write,
+                          has_delta=has_delta, final_boundary=final, eps=s.eps,
+                          out_eps=s.out_eps)
+    torch.cuda.synchronize()
+    assert np.all(down(ws) == 0), "workspace not left zero"
+    return dict(out=down(out), prefix=down(prefix), blocks=down(blocks),
+                aux=None if auxg is None else down(auxg))
+
+
+def split(s, *, final, write=None, has_delta=None):
+    """wsgemm_run then attnres_run on the same inputs (the unfused reading)."""
+    sga = lib()
+    write = s.write if write is None else write
+    has_delta = s.has_delta if has_delta is None else has_delta
+    y = torch.zeros((s.M, s.H), dtype=torch.int16, device=DEV)
+    sga.wsgemm_run(up(s.x), up(s.W), y)
+    prefix, blocks = up(s.prefix), up(s.blocks)
+    out = torch.zeros((s.M, s.H), dtype=torch.int16, device=DEV)
+    aux = torch.zeros((s.M, s.H), dtype=torch.int16, device=DEV)
+    sga.attnres_run(y, prefix, blocks, up(s.norm), up(s.query), up(s.out_norm), out, aux,
+                    nb=s.nb, write=write, has_delta=has_delta, final_boundary=final, eps=s.eps,
+                    out_eps=s.out_eps)
+    torch.cuda.synchronize()
+    return dict(out=down(out), prefix=down(prefix), blocks=down(blocks), aux=down(aux), y=down(y))
+
+
+def check(s, r, *, final, write=None, has_delta=None, aux=True, what=""):
+    write = s.write if write is None else write
+    has_delta = s.has_delta if has_delta is None else has_delta
+    y = oracle.gemm(s.x, s.W, nthreads=16)
+    ref = oracle.attnres(y, s.prefix, s.blocks, s.norm, s.query, s.out_norm, nb=s.nb,
+                         write=write, has_delta=has_delta, final=final, eps=s.eps,
+                         out_eps=s.out_eps, nthreads=16)
+    h = ref.h_exact if not final or s.nb == 0 else bf16_to_f64(torch_round(ref.h_exact))
+    scale = 1.0 / np.sqrt(np.mean(h * h, axis=-1) + np.float32(s.out_eps))
+    assert_fused_out_close(r["out"], ref.out, r["prefix"], ref.prefix, ref.probs[:, s.nb], scale,
+                           s.out_norm, final=final, what=f"{what} out")
+    assert_new_prefix_close(r["prefix"], ref.prefix, s.prefix, has_delta, f"{what} prefix")
+    if aux:
+        assert np.array_equal(r["aux"], r["prefix"]), f"{what} aux != prefix"
+    if write >= 0:
+        assert np.array_equal(r["blocks"][:, write], r["prefix"]), f"{what} written slot"
+    others = [b for b in range(s.blocks.shape[1]) if b != write]
+    assert np.array_equal(r["blocks"][:, others], s.blocks[:, others]), f"{what} untouched slots"
+    return ref
+
+
+def torch_round(h):
+    """float64 -> bfloat16 bits through torch (only to size the tolerance)."""
+    return torch.tensor(h).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.fixture(scope="module")
+def configs():
+    return {c: synth.config_inputs(c) for c in (0, 1, 2)}
+
+
+@pytest.mark.parametrize("final", [0, 1])
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+def test_fused_configs(configs, cfg, final):
+    s = configs[cfg]
+    r = fused(s, final=final)
+    check(s, r, final=final, what=f"cfg{cfg} final={final}")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+def test_fused_equals_gemm_then_attnres(configs, cfg):
+    s = configs[cfg]
+    for final in (0, 1):
+        a, b = fused(s, final=final), split(s, final=final)
+        for k in ("out", "prefix", "blocks", "aux"):
+            assert np.array_equal(a[k], b[k]), f"cfg{cfg} final={final}: {k} differs"
+
+
+@pytest.mark.parametrize("M,K,H,nb,cap,write,has_delta", [
+    (13, 1000, 1024, 3, 4, 3, 1),   # ragged tokens, ragged K, narrower rows
+    (64, 256, 64, 2, 3, 1, 1),      # more owners than GEMM workgroups; write a scored slot
+    (5, 520, 7168, 0, 1, 0, 0),     # nb = 0, delta path off (block-write layer)
+    (17, 4096, 7168, 8, 8, 0, 0),   # overwrite a scored slot, no old prefix
+    (1, 0, 7168, 1, 1, -1, 1),      # K = 0: delta = +0.0
+    (64, 7168, 8192, 8, 9, 8, 1),   # widest rows
+])
+def test_fused_edges(M, K, H, nb, cap, write, has_delta):
+    s = synth.decode_step(M, K, nb, H=H, cap=cap, write=write, has_delta=has_delta, seed=M + K)
+    for final in (0, 1):
+        r = fused(s, final=final, aux=(M % 2 == 1))
+        check(s, r, final=final, aux=(M % 2 == 1), what=f"M={M} K={K} H={H} nb={nb}")
+
+
+def test_fused_back_to_back_reuses_workspace():
+    """Consecutive calls on one workspace: each call leaves the counters at zero."""
+    ws = lib().make_workspace(8, 7168, 4, DEV)
+    for layer in range(3):
+        s = synth.decode_step(8, 2048, 4, layer=layer, seed=5)
+        r = fused(s, final=layer % 2, ws=ws)
+        check(s, r, final=layer % 2, what=f"layer {layer}")
+
+
+def test_fused_deterministic(configs):
+    s = configs[2]
+    a, b = fused(s, final=0), fused(s, final=0)
+    for k in ("out", "prefix", "blocks"):
+        assert np.array_equal(a[k], b[k]), k
