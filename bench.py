@@ -1,0 +1,218 @@
+"""Benchmark of the fused o-projection + AttnRes decode step on one MI355X.
+
+Default workload: M = 8 tokens, K = 4096, N = H = 7168, nb = 4 saved blocks,
+non-write layer (delta path), one aux copy, non-final boundary. One "step" is
+one attnres_oproj_run call (one launch of the fused kernel) over one batch.
+
+Protocol:
+  * L distinct layer copies (W, x, prefix, blocks, out, aux, workspace) with a
+    footprint of at least 640 MB, so the 256 MB Infinity Cache cannot serve W;
+    copy 0 is checked against the FP64 oracle before timing.
+  * `--warmup` eager steps, then one HIP graph holding exactly `--steps` calls
+    that cycle through the copies; the graph is replayed once untimed (upload)
+    and once timed, bracketed by synchronisations and HIP events on the stream
+    the kernels run on.
+  * value = algorithmic bytes per step / measured time per step (GB/s);
+    roofline.achieved is the same figure for the fused kernel, the only kernel
+    of a step, against the 8 TB/s HBM peak.
+  * cpu_baseline: the FP64 oracle (oracle/, plain C) on the same step, timed on
+    the host cores, in the same process.
+
+Prints one JSON line. `--config` picks another fused workload (0: M=1 K=1024
+nb=1; 2: M=64 K=8192 nb=8 with a block write) for side measurements.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FOOTPRINT = 640e6
+
+WORKLOADS = {
+    0: dict(M=1, K=1024, nb=1, cap=1, write=-1, has_delta=1),
+    1: dict(M=8, K=4096, nb=4, cap=4, write=-1, has_delta=1),
+    2: dict(M=64, K=8192, nb=8, cap=9, write=8, has_delta=1),
+}
+H = 7168
+
+
+def algorithmic_bytes(M, K, nb, write, has_delta, aux=1, H=H):
+    """What the step must move, each byte once: W, x, three gain rows, and per
+    token the old prefix (if read), the nb scored blocks, the new prefix, the
+    aux copy, the written block slot and the output row."""
+    row = 2 * H
+    return 2 * H * K + 2 * M * K + 3 * row + M * row * (
+        has_delta + nb + 1 + aux + (1 if write >= 0 else 0) + 1)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, choices=sorted(WORKLOADS))
+    ap.add_argument("--final", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="bounded host time for the oracle baseline (0 skips it)")
+    ap.add_argument("--no-check", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import skinny_gemm_attention_amd as sga
+    import synth
+
+    cfg = WORKLOADS[args.config]
+    M, K, nb, cap, write, has_delta = (cfg[k] for k in ("M", "K", "nb", "cap", "write",
+                                                      "has_delta"))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = synth.decode_step(M, K, nb, cap=cap, write=write, has_delta=has_delta,
+                          final=args.final, seed=0)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    step_bytes = algorithmic_bytes(M, K, nb, write, has_delta)
+    copy_bytes = 2 * H * K + 2 * M * K + M * 2 * H * (4 + cap)
+    L = max(2, math.ceil(FOOTPRINT / copy_bytes))
+    base = dict(x=up(s.x), W=up(s.W), prefix=up(s.prefix), blocks=up(s.blocks))
+    norm, query, out_norm = up(s.norm), up(s.query), up(s.out_norm)
+    layers = []
+    for i in range(L):
+        t = {k: v.clone() for k, v in base.items()}
+        t["out"] = torch.zeros((M, H), dtype=torch.int16, device=dev)
+        t["aux"] = torch.zeros((M, H), dtype=torch.int16, device=dev)
+        t["ws"] = sga.make_workspace(M, H, nb, dev)
+        layers.append(t)
+    torch.cuda.synchronize()
+
+    def step(i):
+        t = layers[i % L]
+        sga.attnres_oproj_run(t["x"], t["W"], t["prefix"], t["blocks"], norm, query, out_norm,
+                              t["out"], t["aux"], t["ws"], nb=nb, write=write,
+                              has_delta=has_delta, final_boundary=args.final)
+
+    # parity of the first call on copy 0 (fresh inputs) against the oracle
+    if not args.no_check:
+        import oracle
+
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from parity_tools import assert_new_prefix_close
+
+        step(0)
+        torch.cuda.synchronize()
+        ref = oracle.attnres_oproj(s.x, s.W, s.prefix, s.blocks, s.norm, s.query, s.out_norm,
+                                   nb=nb, write=write, has_delta=has_delta, final=args.final,
+                                   nthreads=8)
+        got_prefix = layers[0]["prefix"].cpu().numpy().view(np.uint16)
+        assert_new_prefix_close(got_prefix, ref.prefix, s.prefix, has_delta, "bench prefix")
+        o = synth.bf16_bits_to_f32(layers[0]["out"].cpu().numpy().view(np.uint16))
+        r = synth.bf16_bits_to_f32(ref.out)
+        rel = float(np.linalg.norm(o - r) / np.linalg.norm(r))
+        assert rel < 5e-3, f"bench parity: relative L2 {rel}"
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(args.steps):
+                step(i)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph.replay()  # upload / first-launch costs, untimed
+    torch.cuda.synchronize()
+
+    with torch.cuda.stream(stream):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    us_step = ms_total * 1e3 / args.steps
+    gbs = step_bytes / (us_step * 1e-6) / 1e9
+
+    result = {
+        "metric": "µs/layer-step + achieved HBM GB/s (% of peak), o-proj+AttnRes, M=1/8/64",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "us_per_layer_step": round(us_step, 3),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_total / args.steps, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64 normals, bf16)",
+        "config": {
+            "workload": f"fused o-proj + AttnRes, M={M}, K={K}, N=H={H}, nb={nb}, "
+                        f"write={write}, has_delta={has_delta}, aux=1, final={args.final}",
+            "M": M, "K": K, "N": H, "nb": nb, "write": write, "final": args.final,
+            "layer_copies": L, "footprint_MB": round(L * copy_bytes / 1e6, 1),
+            "timing": "one HIP graph of `steps` calls, HIP events on the launch stream",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "fused_kernel (attnres_oproj_run), one launch per step",
+            "algorithmic_bytes_per_launch": step_bytes,
+        },
+    }
+
+    if args.cpu_seconds > 0:
+        import oracle
+
+        cores = len(os.sched_getaffinity(0))
+        threads = min(cores, M)
+        times = []
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            oracle.attnres_oproj(s.x, s.W, s.prefix, s.blocks, s.norm, s.query, s.out_norm,
+                                 nb=nb, write=write, has_delta=has_delta, final=args.final,
+                                 nthreads=threads)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start >= args.cpu_seconds or len(times) >= 200:
+                break
+        t_med = float(np.median(times))
+        result["cpu_baseline"] = {
+            "value": round(step_bytes / t_med / 1e9, 3),
+            "unit": "GB/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(times)} full steps of the same workload (copy 0), median "
+                      f"{t_med * 1e3:.1f} ms/step, FP64 C oracle with {threads} threads "
+                      f"(one per token) of {cores} available",
+            "ms_per_step": round(t_med * 1e3, 2),
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

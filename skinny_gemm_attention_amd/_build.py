@@ -1,7 +1,8 @@
 """Builds libattnres.so (the gfx950 kernels and the C ABI) in the package folder.
 
 hipcc cross-compiles for gfx950 without a GPU. Packed FP32 instructions are
-disabled (``-packed-fp32-ops``); the kernels never rely on them.
+disabled (``-packed-fp32-ops``); the kernels never rely on them. Implicit FP
+contraction is off: every fused multiply-add is written as fmaf.
 """
 from __future__ import annotations
 
@@ -25,6 +26,9 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
+    # no implicit multiply-add contraction: every fused multiply-add is an
+    # explicit fmaf, so all kernels round the shared AttnRes arithmetic alike
+    "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]

@@ -93,6 +93,29 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 
+// Device-scope (agent) 8-byte store and load. On gfx950 these are global
+// stores / loads with the device scope bit (sc1): they are coherent across the
+// L2 caches of the eight XCDs without writing back or invalidating any cache.
+__device__ __forceinline__ void st8_device(void* p, u32x2 v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                     __builtin_bit_cast(unsigned long long, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32x2 ld8_device(const void* p) {
+  return __builtin_bit_cast(
+      u32x2, __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Blocks until every memory operation this wavefront has issued is complete:
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone). A completed device-scope
+// store is visible to device-scope loads from any compute unit.
+__device__ __forceinline__ void wait_vmem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---- fixed-order reductions --------------------------------------------------
 
 template <int CTRL>

@@ -8,18 +8,30 @@
 //     tokens, the matching columns of the new prefix: it rounds its y columns to
 //     bf16 (-0.0 -> +0.0), forms new = bf16(prefix + y) (or y) and stores new
 //     to prefix, aux and, when the written slot is not scored, the block slot;
-//     then it signals `arrive` (release);
-//   * workgroup t < M also owns token t's AttnRes: before its GEMM share it runs
-//     pre() on the token's saved blocks (off the critical path, results in
-//     LDS); after its own signal it waits until every workgroup has arrived
-//     (acquire), reads the token's full new prefix back and runs post().
+//     then it signals `arrive`;
+//   * workgroup t < M also owns token t's AttnRes: while the first stage of its
+//     W loads is in flight it runs pre() on the token's saved blocks (results in
+//     LDS); after its own signal it waits until every workgroup has arrived,
+//     reads the token's full new prefix back and runs post().
 // Only the owners wait, and they wait on workgroups that never wait, so the
 // grid drains whatever the residency. The last owner to pass the wait resets
 // the two counters, leaving the workspace zero for the next call.
+//
+// Hand-off without cache maintenance: the new prefix columns are stored with
+// device-scope stores; each wavefront waits for its stores to complete
+// (s_waitcnt vmcnt(0)) before the workgroup barrier that precedes the
+// counter increment, and the owner reads the columns back with device-scope
+// loads after it has seen the counter reach G (and invalidated its caches once).
+// No L2 write-back is needed: nothing else the owner reads was written in this
+// launch.
 #include "gemm.hpp"
 #include "launch.hpp"
 
 namespace attnres {
+
+#ifndef FUSED_D
+#define FUSED_D(TT) ((TT) == 1 ? 4 : (TT) == 2 ? 4 : 2)
+#endif
 
 template <int RT, int TT, int NW, int D>
 __global__ __launch_bounds__(NW * 64) void fused_kernel(FusedParams f, int R, int G) {
@@ -48,60 +60,104 @@ __global__ __launch_bounds__(NW * 64) void fused_kernel(FusedParams f, int R, in
     if (qvalid && a.has_delta) qprefix = ld8(a.prefix + (size_t)qm * a.ld_prefix + row0 + qr);
   }
 
+  // First stage of this workgroup's W and x loads goes out before anything else.
+  C core;
+  core.start(f.x, f.ldx, f.W, f.ldw, M, f.K, row0, rows);
+
   // ---- owner: pre() of token g, results to LDS --------------------------------
+  // Two passes over the saved blocks keep the register footprint small while the
+  // first W stage is held: the statistics pass, then (after the reduction) the
+  // mixture pass, whose block reads hit in L2.
   PreScalars pre = {0.0f, 0.0f};
   u32x4 gq[NCH];
   if (owner) {
-    u32x4 vb[kMaxBlocks][NCH];
-    float w[NCH][8];
+    const uint16_t* tok_blocks = a.blocks + (size_t)g * a.bst_t;
+    float ps[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ps[k] = 0.0f;
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int c = tid + j * NT;
       const bool valid = c < CH;
       const size_t col = (size_t)c * 8;
-#pragma unroll
-      for (int b = 0; b < kMaxBlocks; ++b)
-        vb[b][j] = (valid && b < a.nb) ? ld16(a.blocks + g * a.bst_t + b * a.bst_b + col) : zero;
       gq[j] = valid ? ld16(a.out_norm + col) : zero;
+      float w[8];
       if (valid) {
-        weights8(a, c, w[j]);
+        weights8(a, c, w);
+        f32x4* pw = reinterpret_cast<f32x4*>(lds_w + c * 8);
+        pw[0] = f32x4{w[0], w[1], w[2], w[3]};
+        pw[1] = f32x4{w[4], w[5], w[6], w[7]};
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w[j][i] = 0.0f;
+        for (int i = 0; i < 8; ++i) w[i] = 0.0f;
+      }
+#pragma unroll
+      for (int b = 0; b < kMaxBlocks; ++b) {
+        if (b < a.nb && valid) {
+          float v[8];
+          unpack8(ld16(tok_blocks + b * a.bst_b + col), v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            ps[b] = __builtin_fmaf(v[i], v[i], ps[b]);
+            ps[8 + b] = __builtin_fmaf(v[i], w[i], ps[8 + b]);
+          }
+        }
       }
     }
-    float mix[NCH][8];
     if (a.nb > 0) {
-      float ps[16];
-      pre_partials(vb, w, a.nb, ps);
       wg_sum<16, NW>(ps, lds_pre);
-      pre = pre_finish(ps, vb, a.nb, a.eps, a.inv_h, mix);
+      float lg[kMaxBlocks], e[kMaxBlocks];
+#pragma unroll
+      for (int b = 0; b < kMaxBlocks; ++b) lg[b] = ps[8 + b] * rstd(ps[b], a.inv_h, a.eps);
+      float m = lg[0];
+#pragma unroll
+      for (int b = 1; b < kMaxBlocks; ++b)
+        if (b < a.nb) m = fmaxf(m, lg[b]);
+      float S = 0.0f;
+#pragma unroll
+      for (int b = 0; b < kMaxBlocks; ++b) {
+        e[b] = b < a.nb ? exp_fast(lg[b] - m) : 0.0f;
+        S += e[b];
+      }
+      pre.maxl = m;
+      pre.S = S;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int c = tid + j * NT;
+        if (c < CH) {
+          const size_t col = (size_t)c * 8;
+          float mix[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) mix[i] = 0.0f;
+#pragma unroll
+          for (int b = 0; b < kMaxBlocks; ++b) {
+            if (b < a.nb) {
+              float v[8];
+              unpack8(ld16(tok_blocks + b * a.bst_b + col), v);
+#pragma unroll
+              for (int i = 0; i < 8; ++i) mix[i] = __builtin_fmaf(e[b], v[i], mix[i]);
+            }
+          }
+          f32x4* pm = reinterpret_cast<f32x4*>(lds_mix + c * 8);
+          pm[0] = f32x4{mix[0], mix[1], mix[2], mix[3]};
+          pm[1] = f32x4{mix[4], mix[5], mix[6], mix[7]};
+        }
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < NCH; ++j)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) mix[j][i] = 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = tid + j * NT;
-      if (c < CH) {
-        f32x4* pm = reinterpret_cast<f32x4*>(lds_mix + c * 8);
-        f32x4* pw = reinterpret_cast<f32x4*>(lds_w + c * 8);
-        pm[0] = f32x4{mix[j][0], mix[j][1], mix[j][2], mix[j][3]};
-        pm[1] = f32x4{mix[j][4], mix[j][5], mix[j][6], mix[j][7]};
-        pw[0] = f32x4{w[j][0], w[j][1], w[j][2], w[j][3]};
-        pw[1] = f32x4{w[j][4], w[j][5], w[j][6], w[j][7]};
+      for (int j = 0; j < NCH; ++j) {
+        const int c = tid + j * NT;
+        if (c < CH) {
+          f32x4* pm = reinterpret_cast<f32x4*>(lds_mix + c * 8);
+          pm[0] = pm[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
       }
     }
   }
 
   // ---- GEMM share: rows [row0, row0 + rows) for all M tokens ---------------------
-  {
-    f32x4 acc[RT][TT];
-    C::accumulate(f.x, f.ldx, f.W, f.ldw, M, f.K, row0, rows, acc);
-    C::stash(red, acc);
-  }
+  core.finish();
+  core.stash(red);
   __syncthreads();
   if (qvalid) {
     const f32x4 s = C::gather(red, tid);
@@ -114,13 +170,13 @@ __global__ __launch_bounds__(NW * 64) void fused_kernel(FusedParams f, int R, in
       nv = u32x2{y01, y23};
     }
     const size_t col = (size_t)(row0 + qr);
-    st8(a.prefix + (size_t)qm * a.ld_prefix + col, nv);
+    st8_device(a.prefix + (size_t)qm * a.ld_prefix + col, nv);  // read back by owner qm
     if (a.aux) st8(a.aux + (size_t)qm * a.ld_aux + col, nv);
     if (a.write >= a.nb) st8(a.blocks + qm * a.bst_t + a.write * a.bst_b + col, nv);
   }
 
   // ---- hand-off: publish this workgroup's columns ---------------------------------
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  wait_vmem();
   __syncthreads();
   if (tid == 0) __hip_atomic_fetch_add(&f.sync->arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!owner) return;
@@ -128,9 +184,9 @@ __global__ __launch_bounds__(NW * 64) void fused_kernel(FusedParams f, int R, in
   if (tid == 0) {
     while (__hip_atomic_load(&f.sync->arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)G)
       __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
   // ---- owner: post() of token g ------------------------------------------------------
   const int t = g;
@@ -140,7 +196,9 @@ __global__ __launch_bounds__(NW * 64) void fused_kernel(FusedParams f, int R, in
   for (int j = 0; j < NCH; ++j) {
     const int c = tid + j * NT;
     if (c < CH) {
-      nbits[j] = ld16(a.prefix + (size_t)t * a.ld_prefix + (size_t)c * 8);
+      const uint16_t* src = a.prefix + (size_t)t * a.ld_prefix + (size_t)c * 8;
+      const u32x2 lo = ld8_device(src), hi = ld8_device(src + 4);
+      nbits[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
       const f32x4* pm = reinterpret_cast<const f32x4*>(lds_mix + c * 8);
       const f32x4* pw = reinterpret_cast<const f32x4*>(lds_w + c * 8);
       const f32x4 m0 = pm[0], m1 = pm[1], w0 = pw[0], w1 = pw[1];
@@ -180,7 +238,7 @@ __global__ __launch_bounds__(NW * 64) void fused_kernel(FusedParams f, int R, in
 template <int RT, int TT>
 static hipError_t go(const FusedParams& p, int R, hipStream_t stream) {
   constexpr int NW = 8;
-  constexpr int D = TT == 1 ? 8 : TT == 2 ? 6 : TT == 3 ? 4 : 3;
+  constexpr int D = FUSED_D(TT);
   const int gemm_wgs = (p.a.H + R - 1) / R;
   const int G = gemm_wgs > p.a.T ? gemm_wgs : p.a.T;
   hipLaunchKernelGGL((fused_kernel<RT, TT, NW, D>), dim3(G), dim3(NW * 64), 0, stream, p, R, G);

@@ -35,26 +35,59 @@ struct GemmCore {
   static constexpr int NT = NW * 64;
   static constexpr int kQuads = RT * TT * 64;  // (tile, lane) pairs of one workgroup tile
 
-  // This wavefront's K range of the workgroup's [R x M] tile, into acc.
-  __device__ static __forceinline__ void accumulate(const uint16_t* __restrict__ x, int64_t ldx,
-                                                    const uint16_t* __restrict__ W, int64_t ldw,
-                                                    int M, int K, int row0, int rows,
-                                                    f32x4 (&acc)[RT][TT]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r16 = lane & 15, kq = lane >> 4;
-    const int S = (K + 31) >> 5;
-    const int s0 = (S * wave) / NW, s1 = (S * (wave + 1)) / NW;
+  // Per-wavefront streaming state. start() computes the operand addresses and
+  // issues the first stage of loads; finish() runs the pipelined K loop, so a
+  // caller can put other work between the two while those loads are in flight.
+  const uint16_t* wp[RT];
+  const uint16_t* xp[TT];
+  bool wv[RT], xv[TT];
+  int s, s1, kq, K;
+  u32x4 wa[D][RT], xa[D][TT], wb[D][RT], xb[D][TT];
+  f32x4 acc[RT][TT];
 
-    const uint16_t* wp[RT];
-    bool wv[RT];
+  __device__ __forceinline__ void load(u32x4 (&wr)[D][RT], u32x4 (&xr)[D][TT], int st) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      // this lane's 8 elements start at k; K % 8 == 0, so k < K implies k + 8 <= K
+      const int k = (st + d) * 32 + kq * 8;
+      const bool kv = (st + d < s1) && (k < K);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) wr[d][rt] = (kv && wv[rt]) ? ld16_stream(wp[rt] + k) : zero;
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) xr[d][tt] = (kv && xv[tt]) ? ld16(xp[tt] + k) : zero;
+    }
+  }
+
+  __device__ __forceinline__ void mma(const u32x4 (&wr)[D][RT], const u32x4 (&xr)[D][TT], int st) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (st + d < s1) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = mfma_bf16(wr[d][rt], xr[d][tt], acc[rt][tt]);
+      }
+    }
+  }
+
+  // This wavefront's K range of the workgroup's [rows x M] tile.
+  __device__ __forceinline__ void start(const uint16_t* __restrict__ x, int64_t ldx,
+                                        const uint16_t* __restrict__ W, int64_t ldw, int M,
+                                        int K_, int row0, int rows) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15;
+    kq = lane >> 4;
+    K = K_;
+    const int S = (K + 31) >> 5;
+    s = (S * wave) / NW;
+    s1 = (S * (wave + 1)) / NW;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int r = rt * 16 + r16;
       wv[rt] = r < rows;
       wp[rt] = W + (size_t)(row0 + (wv[rt] ? r : 0)) * ldw;
     }
-    const uint16_t* xp[TT];
-    bool xv[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
       const int m = tt * 16 + r16;
@@ -65,36 +98,10 @@ struct GemmCore {
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    u32x4 wa[D][RT], xa[D][TT], wb[D][RT], xb[D][TT];
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-
-    auto load = [&](u32x4(&wr)[D][RT], u32x4(&xr)[D][TT], int s) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        // this lane's 8 elements start at k; K % 8 == 0, so k < K implies k + 8 <= K
-        const int k = (s + d) * 32 + kq * 8;
-        const bool kv = (s + d < s1) && (k < K);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) wr[d][rt] = (kv && wv[rt]) ? ld16_stream(wp[rt] + k) : zero;
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) xr[d][tt] = (kv && xv[tt]) ? ld16(xp[tt] + k) : zero;
-      }
-    };
-    auto mma = [&](const u32x4(&wr)[D][RT], const u32x4(&xr)[D][TT], int s) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        if (s + d < s1) {
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = mfma_bf16(wr[d][rt], xr[d][tt], acc[rt][tt]);
-        }
-      }
-    };
-
-    int s = s0;
     if (s < s1) load(wa, xa, s);
+  }
+
+  __device__ __forceinline__ void finish() {
     while (s < s1) {
       if (s + D < s1) load(wb, xb, s + D);
       mma(wa, xa, s);
@@ -107,7 +114,7 @@ struct GemmCore {
   }
 
   // Writes this wavefront's partial tile to LDS: red[((wave*RT + rt)*TT + tt)*64 + lane].
-  __device__ static __forceinline__ void stash(f32x4* red, const f32x4 (&acc)[RT][TT]) {
+  __device__ __forceinline__ void stash(f32x4* red) const {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)

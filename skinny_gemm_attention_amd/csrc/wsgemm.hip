@@ -11,9 +11,10 @@ __global__ __launch_bounds__(NW * 64) void wsgemm_kernel(GemmParams p, int R) {
   __shared__ f32x4 red[NW * C::kQuads];
   const int row0 = blockIdx.x * R;
   const int rows = min(R, p.N - row0);
-  f32x4 acc[RT][TT];
-  C::accumulate(p.x, p.ldx, p.W, p.ldw, p.M, p.K, row0, rows, acc);
-  C::stash(red, acc);
+  C core;
+  core.start(p.x, p.ldx, p.W, p.ldw, p.M, p.K, row0, rows);
+  core.finish();
+  core.stash(red);
   __syncthreads();
   for (int q = threadIdx.x; q < C::kQuads; q += C::NT) {
     int m, r;
