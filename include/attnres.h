@@ -116,10 +116,22 @@ int wsgemm_run(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, 
 
 /*
  * attnres_oproj_workspace_size - bytes of device workspace attnres_oproj_run
- * needs for M tokens, hidden width H and nb saved blocks. The workspace must be
- * zero-filled once when it is allocated; every call leaves it zero again.
+ * needs for M tokens and hidden width H (nb does not change it): a 256-byte
+ * header and one bf16 mailbox row per token.
  */
 size_t attnres_oproj_workspace_size(int M, int H, int nb);
+
+/*
+ * attnres_oproj_workspace_init - prepares a workspace once, after allocation:
+ * zeroes the header and arms every mailbox word (enqueued on `stream`).
+ * Every attnres_oproj_run call leaves the workspace armed again. The first
+ * 32-bit word of the header becomes nonzero if a call ever gave up waiting
+ * for its own workgroups (a safety bound of about a second per wait that a
+ * healthy device never reaches); that call's outputs are then invalid.
+ *   workspace: device memory, 256-byte aligned; bytes: a multiple of 4, at
+ *   least 256.
+ */
+int attnres_oproj_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attnres_oproj_run - the fused decode step: the o-projection of x (the
@@ -131,9 +143,9 @@ size_t attnres_oproj_workspace_size(int M, int H, int nb);
  *   x [M, K] row stride ldx; W [H, K] row stride ldw; 1 <= M <= 64;
  *   K >= 0, K % 8 == 0 (K == 0: delta = +0.0, x and W unused and may be NULL);
  *   H as for attnres_run.
- *   workspace: device memory of at least attnres_oproj_workspace_size(M, H, nb)
- *   bytes, 256-byte aligned, zero-filled at allocation; calls that may run at
- *   the same time need distinct workspaces.
+ *   workspace: at least attnres_oproj_workspace_size(M, H, nb) bytes, 256-byte
+ *   aligned, prepared once by attnres_oproj_workspace_init; calls that may run
+ *   at the same time need distinct workspaces.
  */
 int attnres_oproj_run(const void* x, int64_t ldx, const void* W, int64_t ldw, int K, void* prefix,
                       int64_t ld_prefix, void* blocks, int64_t blk_stride_t,

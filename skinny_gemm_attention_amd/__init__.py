@@ -32,6 +32,8 @@ _lib.attnres_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I, _P, _P, _P,
 _lib.wsgemm_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I, _I, _I, _P]
 _lib.attnres_oproj_workspace_size.argtypes = [_I, _I, _I]
 _lib.attnres_oproj_workspace_size.restype = _SZ
+_lib.attnres_oproj_workspace_init.argtypes = [_P, _SZ, _P]
+_lib.attnres_oproj_workspace_init.restype = _I
 _lib.attnres_oproj_run.argtypes = [_P, _I64, _P, _I64, _I, _P, _I64, _P, _I64, _I64, _I, _P, _P,
                                    _P, _P, _I64, _P, _I64, _F, _F, _I, _I, _I, _I, _I, _I, _P,
                                    _SZ, _P]
@@ -41,7 +43,7 @@ for _f in (_lib.attnres_run, _lib.wsgemm_run, _lib.attnres_oproj_run):
     _f.restype = _I
 
 EXPORTS = ("attnres_run", "wsgemm_run", "attnres_oproj_run", "attnres_oproj_workspace_size",
-           "attnres_strerror")
+           "attnres_oproj_workspace_init", "attnres_strerror")
 
 
 class AttnResError(RuntimeError):
@@ -118,9 +120,19 @@ def attnres_oproj_workspace_size(M: int, H: int, nb: int) -> int:
     return int(_lib.attnres_oproj_workspace_size(M, H, nb))
 
 
+def attnres_oproj_workspace_init(workspace, stream=None):
+    """Arms a workspace once after allocation (see attnres_oproj_workspace_init)."""
+    rc = _lib.attnres_oproj_workspace_init(ctypes.c_void_p(workspace.data_ptr()),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream(stream))
+    _check(rc, "attnres_oproj_workspace_init")
+    return workspace
+
+
 def make_workspace(M: int, H: int, nb: int, device="cuda") -> torch.Tensor:
-    """Zero-filled workspace for attnres_oproj_run (torch allocates it)."""
-    return torch.zeros(attnres_oproj_workspace_size(M, H, nb), dtype=torch.uint8, device=device)
+    """A workspace for attnres_oproj_run: torch allocates it, the library arms it."""
+    ws = torch.empty(attnres_oproj_workspace_size(M, H, nb), dtype=torch.uint8, device=device)
+    return attnres_oproj_workspace_init(ws)
 
 
 def attnres_oproj_run(x, W, prefix, blocks, norm, query, out_norm, out, aux, workspace, *, nb,

@@ -77,7 +77,12 @@ AttnParams make_params(const void* delta, int64_t ld_delta, void* prefix, int64_
   return p;
 }
 
-constexpr size_t kWorkspaceBytes = 256;
+// Header plus one bf16 mailbox row per token.
+size_t workspace_bytes_for(int M, int H) {
+  if (M < 0 || H < 0) return 0;
+  const size_t mailbox = (size_t)M * (size_t)H * 2;
+  return attnres::kWorkspaceHeader + ((mailbox + 255) & ~(size_t)255);
+}
 
 }  // namespace
 
@@ -128,10 +133,16 @@ int wsgemm_run(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, 
 }
 
 size_t attnres_oproj_workspace_size(int M, int H, int nb) {
-  (void)M;
-  (void)H;
   (void)nb;
-  return kWorkspaceBytes;
+  return workspace_bytes_for(M, H);
+}
+
+int attnres_oproj_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes < attnres::kWorkspaceHeader) return ATTNRES_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) || (workspace_bytes & 3u))
+    return ATTNRES_EWORKSPACE;
+  return from_hip(attnres::launch_workspace_init(workspace, workspace_bytes,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 int attnres_oproj_run(const void* x, int64_t ldx, const void* W, int64_t ldw, int K, void* prefix,
@@ -151,7 +162,7 @@ int attnres_oproj_run(const void* x, int64_t ldx, const void* W, int64_t ldw, in
   if (K > 0 && (ldx < K || ldw < K)) return ATTNRES_EINVAL;
   if (K > 0 && (!aligned16(x) || !aligned16(W))) return ATTNRES_EALIGN;
   if (K > 0 && (!stride8(ldx) || !stride8(ldw))) return ATTNRES_EALIGN;
-  if (!workspace || workspace_bytes < kWorkspaceBytes ||
+  if (!workspace || workspace_bytes < workspace_bytes_for(M, H) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return ATTNRES_EWORKSPACE;
   attnres::FusedParams p;
@@ -163,7 +174,8 @@ int attnres_oproj_run(const void* x, int64_t ldx, const void* W, int64_t ldw, in
   p.W = static_cast<const uint16_t*>(W);
   p.ldw = ldw;
   p.K = K;
-  p.sync = static_cast<attnres::FusedSync*>(workspace);
+  p.ws = static_cast<attnres::FusedWorkspace*>(workspace);
+  p.mailbox = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + attnres::kWorkspaceHeader);
   return from_hip(attnres::launch_fused(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
 }
 
 hipError_t launch_attnres(const AttnParams& p, hipStream_t stream) {
-  constexpr int NT = 512;
+  constexpr int NT = kTokenThreads;
   hipLaunchKernelGGL((attnres_kernel<NT>), dim3(p.T), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }

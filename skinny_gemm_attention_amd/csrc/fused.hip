@@ -3,264 +3,267 @@
 // delta of the same layer; attn_res.kernel page: ClusterAttnRes; gemm.ws_gemm
 // page: WsGemm).
 //
-// Roles inside one grid of G = max(ceil(H / R), M) workgroups:
-//   * every workgroup g owns rows [g R, g R + R) of W (the GEMM) and, for all M
-//     tokens, the matching columns of the new prefix: it rounds its y columns to
-//     bf16 (-0.0 -> +0.0), forms new = bf16(prefix + y) (or y) and stores new
-//     to prefix, aux and, when the written slot is not scored, the block slot;
-//     then it signals `arrive`;
-//   * workgroup t < M also owns token t's AttnRes: while the first stage of its
-//     W loads is in flight it runs pre() on the token's saved blocks (results in
-//     LDS); after its own signal it waits until every workgroup has arrived,
-//     reads the token's full new prefix back and runs post().
-// Only the owners wait, and they wait on workgroups that never wait, so the
-// grid drains whatever the residency. The last owner to pass the wait resets
-// the two counters, leaving the workspace zero for the next call.
+// One grid of 512-thread workgroups, two roles:
+//   * GEMM workgroups g < G each own rows [g R, g R + R) of W and, for all M
+//     tokens, the matching columns of the new prefix: they round their y
+//     columns to bf16 (-0.0 -> +0.0), form new = bf16(prefix + y) (or y), store
+//     new to prefix, aux and, when the written slot is not scored, the block
+//     slot, and post it to the token's mailbox row. They never wait.
+//   * Owner workgroups G + o (o < NO) own tokens o, o + NO, ... (at most four):
+//     they run pre() on each token's saved blocks while the GEMM workgroups
+//     stream W (ClusterAttnRes.state: pre needs nothing the GEMM produces),
+//     then collect each token's new prefix from its mailbox row and run post().
+// R (even, at most 32) is chosen so that G + NO fits the compute units (for
+// H = 7168: 239 GEMM workgroups of 30 rows): the owners' saved-block reads then
+// overlap the W stream on units of their own instead of extending it. Owners
+// are the highest workgroup ids and wait only on workgroups that never wait,
+// so the grid drains whatever the residency.
 //
-// Hand-off without cache maintenance: the new prefix columns are stored with
-// device-scope stores; each wavefront waits for its stores to complete
-// (s_waitcnt vmcnt(0)) before the workgroup barrier that precedes the
-// counter increment, and the owner reads the columns back with device-scope
-// loads after it has seen the counter reach G (and invalidated its caches once).
-// No L2 write-back is needed: nothing else the owner reads was written in this
-// launch.
+// Mailbox hand-off (the sentinel scheme of the pages' Lamport mailboxes,
+// oproj.prepared page and positive_zero on the gemm.ws_gemm page): every
+// mailbox word holds the bf16 pair (+0.0, -0.0) between calls. A new-prefix
+// pair never contains -0.0 (the delta's -0.0 is made +0.0 and a bf16 sum
+// that is zero is +0.0), so a word differs from the sentinel exactly when its
+// value has arrived. GEMM workgroups write each pair once with a device-scope
+// (sc1) store; each owner thread polls its own 8-column chunks with
+// device-scope loads, in a fixed chunk order, and re-arms them after reading.
+// One memory latency separates a store from its consumer; no counter, fence or
+// cache write-back is involved. A spin limit bounds every wait: an owner that
+// gives up records it in the workspace header and finishes.
 #include "gemm.hpp"
 #include "launch.hpp"
 
 namespace attnres {
 
+constexpr int kMaxTokensPerOwner = 4;
+
 #ifndef FUSED_D
-#define FUSED_D(TT) ((TT) == 1 ? 4 : (TT) == 2 ? 4 : 2)
+#define FUSED_D(TT) ((TT) == 1 ? 8 : (TT) == 2 ? 6 : (TT) == 3 ? 4 : 3)
 #endif
 
-template <int RT, int TT, int NW, int D>
-__global__ __launch_bounds__(NW * 64) void fused_kernel(FusedParams f, int R, int G) {
+__device__ __forceinline__ void st4_device(void* p, unsigned v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Polls one 8-column chunk (four words) of a mailbox row until no word holds
+// the sentinel; gives up after kSpinLimit rounds (about a second), flagging
+// the workspace, so every wave terminates.
+constexpr int kSpinLimit = 1 << 20;
+__device__ __forceinline__ u32x4 collect_chunk(const unsigned* p, FusedWorkspace* ws) {
+  u32x2 lo, hi;
+  for (int spin = 0;; ++spin) {
+    lo = ld8_device(p);
+    hi = ld8_device(p + 2);
+    if (lo.x != kMailboxSentinel && lo.y != kMailboxSentinel && hi.x != kMailboxSentinel &&
+        hi.y != kMailboxSentinel)
+      break;
+    if (spin >= kSpinLimit) {
+      __hip_atomic_store(&ws->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+template <int RT, int TT, int D>
+__global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int R, int G, int NO) {
+  constexpr int NT = kTokenThreads, NW = NT / 64;
   using C = GemmCore<RT, TT, NW, D>;
-  constexpr int NT = NW * 64;
   constexpr int NCH = TokenShape<NT>::NCH;
-  __shared__ f32x4 red[NW * C::kQuads];
-  __shared__ float lds_mix[kMaxH], lds_w[kMaxH];
+  union Smem {
+    f32x4 red[NW * C::kQuads];
+    float mix[kMaxTokensPerOwner][kMaxH];
+  };
+  __shared__ Smem sm;
   __shared__ float lds_pre[NW * 16], lds_post[NW * 4], lds_fin[NW];
 
   const AttnParams& a = f.a;
   const int g = blockIdx.x, tid = threadIdx.x, CH = a.H >> 3;
   const int M = a.T;
-  const bool owner = g < M;
-  const int row0 = g * R;
-  const int rows = row0 < a.H ? min(R, a.H - row0) : 0;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  // This thread's quad of the GEMM epilogue and its old prefix (prefetched).
-  int qm = 0, qr = 0;
-  bool qvalid = false;
-  u32x2 qprefix = {0u, 0u};
-  if (tid < C::kQuads) {
-    C::quad_coords(tid, qm, qr);
-    qvalid = qm < M && qr < rows;
-    if (qvalid && a.has_delta) qprefix = ld8(a.prefix + (size_t)qm * a.ld_prefix + row0 + qr);
-  }
-
-  // First stage of this workgroup's W and x loads goes out before anything else.
-  C core;
-  core.start(f.x, f.ldx, f.W, f.ldw, M, f.K, row0, rows);
-
-  // ---- owner: pre() of token g, results to LDS --------------------------------
-  // Two passes over the saved blocks keep the register footprint small while the
-  // first W stage is held: the statistics pass, then (after the reduction) the
-  // mixture pass, whose block reads hit in L2.
-  PreScalars pre = {0.0f, 0.0f};
-  u32x4 gq[NCH];
-  if (owner) {
-    const uint16_t* tok_blocks = a.blocks + (size_t)g * a.bst_t;
-    float ps[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) ps[k] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = tid + j * NT;
-      const bool valid = c < CH;
-      const size_t col = (size_t)c * 8;
-      gq[j] = valid ? ld16(a.out_norm + col) : zero;
-      float w[8];
-      if (valid) {
-        weights8(a, c, w);
-        f32x4* pw = reinterpret_cast<f32x4*>(lds_w + c * 8);
-        pw[0] = f32x4{w[0], w[1], w[2], w[3]};
-        pw[1] = f32x4{w[4], w[5], w[6], w[7]};
+  if (g < G) {
+    // ---- GEMM role: rows [row0, row0 + rows) for all M tokens -----------------------
+    const int row0 = g * R;
+    const int rows = min(R, a.H - row0);
+    int qm = 0, qr = 0;
+    bool qvalid = false;
+    u32x2 qprefix = {0u, 0u};
+    if (tid < C::kQuads) {
+      C::quad_coords(tid, qm, qr);
+      qvalid = qm < M && qr < rows;
+      if (qvalid && a.has_delta) {
+        const uint16_t* src = a.prefix + (size_t)qm * a.ld_prefix + row0 + qr;
+        qprefix.x = *reinterpret_cast<const unsigned*>(src);
+        if (qr + 2 < rows) qprefix.y = *reinterpret_cast<const unsigned*>(src + 2);
+      }
+    }
+    {
+      C core;
+      core.start(f.x, f.ldx, f.W, f.ldw, M, f.K, row0, rows);
+      core.finish();
+      core.stash(sm.red);
+    }
+    __syncthreads();
+    if (qvalid) {
+      const f32x4 s = C::gather(sm.red, tid);
+      const unsigned y01 = positive_zero(pack2(s.x, s.y)), y23 = positive_zero(pack2(s.z, s.w));
+      u32x2 nv;
+      if (a.has_delta) {
+        nv.x = pack2(add_round_odd(bf_lo(qprefix.x), bf_lo(y01)), add_round_odd(bf_hi(qprefix.x), bf_hi(y01)));
+        nv.y = pack2(add_round_odd(bf_lo(qprefix.y), bf_lo(y23)), add_round_odd(bf_hi(qprefix.y), bf_hi(y23)));
       } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = 0.0f;
+        nv = u32x2{y01, y23};
       }
-#pragma unroll
-      for (int b = 0; b < kMaxBlocks; ++b) {
-        if (b < a.nb && valid) {
-          float v[8];
-          unpack8(ld16(tok_blocks + b * a.bst_b + col), v);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            ps[b] = __builtin_fmaf(v[i], v[i], ps[b]);
-            ps[8 + b] = __builtin_fmaf(v[i], w[i], ps[8 + b]);
-          }
-        }
-      }
+      unsigned* box = f.mailbox + (size_t)qm * (a.H >> 1) + ((row0 + qr) >> 1);
+      st4_device(box, nv.x);  // collected by token qm's owner
+      if (qr + 2 < rows) st4_device(box + 1, nv.y);
+      store_quad_pairs(a.prefix + (size_t)qm * a.ld_prefix + row0, qr, rows, nv);
+      if (a.aux) store_quad_pairs(a.aux + (size_t)qm * a.ld_aux + row0, qr, rows, nv);
+      if (a.write >= a.nb) store_quad_pairs(a.blocks + qm * a.bst_t + a.write * a.bst_b + row0, qr, rows, nv);
     }
-    if (a.nb > 0) {
-      wg_sum<16, NW>(ps, lds_pre);
-      float lg[kMaxBlocks], e[kMaxBlocks];
+    return;
+  }
+
+  // ---- owner role: tokens o, o + NO, ... --------------------------------------------
+  const int o = g - G;
+  int ntok = 0;
 #pragma unroll
-      for (int b = 0; b < kMaxBlocks; ++b) lg[b] = ps[8 + b] * rstd(ps[b], a.inv_h, a.eps);
-      float m = lg[0];
+  for (int k = 0; k < kMaxTokensPerOwner; ++k)
+    if (o + k * NO < M) ntok = k + 1;
+
+  u32x4 gq[NCH];
+  float w[NCH][8];
+  token_weights<NT, NCH>(a, w, gq);
+  PreScalars pre[kMaxTokensPerOwner];
 #pragma unroll
-      for (int b = 1; b < kMaxBlocks; ++b)
-        if (b < a.nb) m = fmaxf(m, lg[b]);
-      float S = 0.0f;
-#pragma unroll
-      for (int b = 0; b < kMaxBlocks; ++b) {
-        e[b] = b < a.nb ? exp_fast(lg[b] - m) : 0.0f;
-        S += e[b];
-      }
-      pre.maxl = m;
-      pre.S = S;
+  for (int k = 0; k < kMaxTokensPerOwner; ++k) {
+    pre[k] = PreScalars{0.0f, 0.0f};
+    if (k < ntok) {
+      float mix[NCH][8];
+      pre[k] = token_pre<NT, NCH>(a, o + k * NO, w, mix, lds_pre);
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int c = tid + j * NT;
         if (c < CH) {
-          const size_t col = (size_t)c * 8;
-          float mix[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) mix[i] = 0.0f;
-#pragma unroll
-          for (int b = 0; b < kMaxBlocks; ++b) {
-            if (b < a.nb) {
-              float v[8];
-              unpack8(ld16(tok_blocks + b * a.bst_b + col), v);
-#pragma unroll
-              for (int i = 0; i < 8; ++i) mix[i] = __builtin_fmaf(e[b], v[i], mix[i]);
-            }
-          }
-          f32x4* pm = reinterpret_cast<f32x4*>(lds_mix + c * 8);
-          pm[0] = f32x4{mix[0], mix[1], mix[2], mix[3]};
-          pm[1] = f32x4{mix[4], mix[5], mix[6], mix[7]};
+          f32x4* pm = reinterpret_cast<f32x4*>(sm.mix[k] + c * 8);
+          pm[0] = f32x4{mix[j][0], mix[j][1], mix[j][2], mix[j][3]};
+          pm[1] = f32x4{mix[j][4], mix[j][5], mix[j][6], mix[j][7]};
         }
       }
-    } else {
+      __syncthreads();  // lds_pre is reused by the next token
+    }
+  }
+
+#pragma unroll
+  for (int k = 0; k < kMaxTokensPerOwner; ++k) {
+    if (k < ntok) {
+      const int t = o + k * NO;
+      unsigned* box = f.mailbox + (size_t)t * (a.H >> 1);
+      u32x4 nbits[NCH];
+      float nw[NCH][8], mix[NCH][8];
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int c = tid + j * NT;
         if (c < CH) {
-          f32x4* pm = reinterpret_cast<f32x4*>(lds_mix + c * 8);
-          pm[0] = pm[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          nbits[j] = collect_chunk(box + c * 4, f.ws);
+          // re-arm for the next call (device scope, like every mailbox access)
+          st8_device(box + c * 4, u32x2{kMailboxSentinel, kMailboxSentinel});
+          st8_device(box + c * 4 + 2, u32x2{kMailboxSentinel, kMailboxSentinel});
+          const f32x4* pm = reinterpret_cast<const f32x4*>(sm.mix[k] + c * 8);
+          const f32x4 m0 = pm[0], m1 = pm[1];
+          mix[j][0] = m0.x; mix[j][1] = m0.y; mix[j][2] = m0.z; mix[j][3] = m0.w;
+          mix[j][4] = m1.x; mix[j][5] = m1.y; mix[j][6] = m1.z; mix[j][7] = m1.w;
+        } else {
+          nbits[j] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) mix[j][i] = 0.0f;
+        }
+        unpack8(nbits[j], nw[j]);
+      }
+      float pp[4];
+      post_partials(nw, w, mix, pp);
+      wg_sum<4, NW>(pp, lds_post);
+      if (a.write >= 0 && a.write < a.nb) {  // a scored slot: written after pre() read it
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          const int c = tid + j * NT;
+          if (c < CH) st16(a.blocks + t * a.bst_t + a.write * a.bst_b + (size_t)c * 8, nbits[j]);
         }
       }
+      finish_out<NT, NCH>(a, t, pre[k], pp, nw, mix, gq, lds_fin);
+      __syncthreads();  // lds_post / lds_fin are reused by the next token
     }
   }
-
-  // ---- GEMM share: rows [row0, row0 + rows) for all M tokens ---------------------
-  core.finish();
-  core.stash(red);
-  __syncthreads();
-  if (qvalid) {
-    const f32x4 s = C::gather(red, tid);
-    const unsigned y01 = positive_zero(pack2(s.x, s.y)), y23 = positive_zero(pack2(s.z, s.w));
-    u32x2 nv;
-    if (a.has_delta) {
-      nv.x = pack2(add_round_odd(bf_lo(qprefix.x), bf_lo(y01)), add_round_odd(bf_hi(qprefix.x), bf_hi(y01)));
-      nv.y = pack2(add_round_odd(bf_lo(qprefix.y), bf_lo(y23)), add_round_odd(bf_hi(qprefix.y), bf_hi(y23)));
-    } else {
-      nv = u32x2{y01, y23};
-    }
-    const size_t col = (size_t)(row0 + qr);
-    st8_device(a.prefix + (size_t)qm * a.ld_prefix + col, nv);  // read back by owner qm
-    if (a.aux) st8(a.aux + (size_t)qm * a.ld_aux + col, nv);
-    if (a.write >= a.nb) st8(a.blocks + qm * a.bst_t + a.write * a.bst_b + col, nv);
-  }
-
-  // ---- hand-off: publish this workgroup's columns ---------------------------------
-  wait_vmem();
-  __syncthreads();
-  if (tid == 0) __hip_atomic_fetch_add(&f.sync->arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (!owner) return;
-
-  if (tid == 0) {
-    while (__hip_atomic_load(&f.sync->arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)G)
-      __builtin_amdgcn_s_sleep(1);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
-  __syncthreads();
-
-  // ---- owner: post() of token g ------------------------------------------------------
-  const int t = g;
-  u32x4 nbits[NCH];
-  float nw[NCH][8], w[NCH][8], mix[NCH][8];
-#pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = tid + j * NT;
-    if (c < CH) {
-      const uint16_t* src = a.prefix + (size_t)t * a.ld_prefix + (size_t)c * 8;
-      const u32x2 lo = ld8_device(src), hi = ld8_device(src + 4);
-      nbits[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
-      const f32x4* pm = reinterpret_cast<const f32x4*>(lds_mix + c * 8);
-      const f32x4* pw = reinterpret_cast<const f32x4*>(lds_w + c * 8);
-      const f32x4 m0 = pm[0], m1 = pm[1], w0 = pw[0], w1 = pw[1];
-      mix[j][0] = m0.x; mix[j][1] = m0.y; mix[j][2] = m0.z; mix[j][3] = m0.w;
-      mix[j][4] = m1.x; mix[j][5] = m1.y; mix[j][6] = m1.z; mix[j][7] = m1.w;
-      w[j][0] = w0.x; w[j][1] = w0.y; w[j][2] = w0.z; w[j][3] = w0.w;
-      w[j][4] = w1.x; w[j][5] = w1.y; w[j][6] = w1.z; w[j][7] = w1.w;
-    } else {
-      nbits[j] = zero;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mix[j][i] = w[j][i] = 0.0f;
-    }
-    unpack8(nbits[j], nw[j]);
-  }
-  // every owner is past the wait once `done` reaches M: the last one resets
-  if (tid == 0) {
-    const unsigned d = __hip_atomic_fetch_add(&f.sync->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d == (unsigned)M - 1u) {
-      __hip_atomic_store(&f.sync->arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&f.sync->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-
-  float pp[4];
-  post_partials(nw, w, mix, pp);
-  wg_sum<4, NW>(pp, lds_post);
-  if (a.write >= 0 && a.write < a.nb) {  // a scored slot: written after pre() read it
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = tid + j * NT;
-      if (c < CH) st16(a.blocks + t * a.bst_t + a.write * a.bst_b + (size_t)c * 8, nbits[j]);
-    }
-  }
-  finish_out<NT, NCH>(a, t, pre, pp, nw, mix, gq, lds_fin);
 }
 
-template <int RT, int TT>
-static hipError_t go(const FusedParams& p, int R, hipStream_t stream) {
-  constexpr int NW = 8;
-  constexpr int D = FUSED_D(TT);
-  const int gemm_wgs = (p.a.H + R - 1) / R;
-  const int G = gemm_wgs > p.a.T ? gemm_wgs : p.a.T;
-  hipLaunchKernelGGL((fused_kernel<RT, TT, NW, D>), dim3(G), dim3(NW * 64), 0, stream, p, R, G);
+__global__ void workspace_init_kernel(unsigned* ws, size_t words) {
+  const size_t header = kWorkspaceHeader / 4;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < words;
+       i += (size_t)gridDim.x * blockDim.x)
+    ws[i] = i < header ? 0u : kMailboxSentinel;
+}
+
+hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t stream) {
+  const size_t words = bytes / 4;
+  const int blocks = (int)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024);
+  hipLaunchKernelGGL(workspace_init_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream,
+                     static_cast<unsigned*>(ws), words);
   return hipGetLastError();
 }
 
+namespace {
+
+int compute_units() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int RT, int TT>
+hipError_t go(const FusedParams& p, int R, int G, int NO, hipStream_t stream) {
+  constexpr int D = FUSED_D(TT);
+  hipLaunchKernelGGL((fused_kernel<RT, TT, D>), dim3(G + NO), dim3(kTokenThreads), 0, stream, p, R, G,
+                     NO);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_fused(const FusedParams& p, hipStream_t stream) {
-  const int R = gemm_rows_per_wg(p.a.H);
-  const int tt = (p.a.T + 15) / 16;
+  const int H = p.a.H, M = p.a.T;
+  // owners: one token each up to 16 tokens, then up to four tokens each
+  const int per_owner = M <= 16 ? 1 : (M + 15) / 16;
+  const int NO = (M + per_owner - 1) / per_owner;
+  // GEMM rows per workgroup: even, at most 32, leaving NO compute units free
+  int room = compute_units() - NO;
+  if (room < 1) room = 1;
+  int R = (H + room - 1) / room;
+  R = (R + 1) & ~1;
+  if (R < 2) R = 2;
+  if (R > 32) R = 32;
+  const int G = (H + R - 1) / R;
+  const int tt = (M + 15) / 16;
   if (R > 16) {
     switch (tt) {
-      case 1: return go<2, 1>(p, R, stream);
-      case 2: return go<2, 2>(p, R, stream);
-      case 3: return go<2, 3>(p, R, stream);
-      default: return go<2, 4>(p, R, stream);
+      case 1: return go<2, 1>(p, R, G, NO, stream);
+      case 2: return go<2, 2>(p, R, G, NO, stream);
+      case 3: return go<2, 3>(p, R, G, NO, stream);
+      default: return go<2, 4>(p, R, G, NO, stream);
     }
   }
   switch (tt) {
-    case 1: return go<1, 1>(p, R, stream);
-    case 2: return go<1, 2>(p, R, stream);
-    case 3: return go<1, 3>(p, R, stream);
-    default: return go<1, 4>(p, R, stream);
+    case 1: return go<1, 1>(p, R, G, NO, stream);
+    case 2: return go<1, 2>(p, R, G, NO, stream);
+    case 3: return go<1, 3>(p, R, G, NO, stream);
+    default: return go<1, 4>(p, R, G, NO, stream);
   }
 }
 

@@ -4,9 +4,10 @@
 // page, module summary) for M <= 64 tokens: BF16 operands, FP32 accumulation,
 // K partial sums added in K order. The layout is ours:
 //
-//   * A workgroup owns R consecutive rows of W (R = 4..32, a multiple of 4) and
-//     all K; its NW wavefronts split K into NW consecutive ranges of 32-wide
-//     k-steps.
+//   * A workgroup owns R consecutive rows of W (R = 4..32, a multiple of 4: 256
+//     workgroups of 28 rows for 7168 rows) and all K; its NW wavefronts split K
+//     into NW consecutive ranges of 32-wide k-steps. Each x fragment a
+//     wavefront loads serves all of the workgroup's rows.
 //   * Per k-step a wavefront issues v_mfma_f32_16x16x32_bf16 with W as the A
 //     operand (16 rows x 32 k) and x as the B operand (32 k x 16 tokens), one
 //     MFMA per (16-row tile rt < RT, 16-token tile tt < TT). Lane l loads 16
@@ -138,14 +139,21 @@ struct GemmCore {
   }
 };
 
-// Rows of W per workgroup for N output rows: spread N over 256 compute units,
-// a multiple of 4, at most 32 (two 16-row MFMA tiles).
+// Rows of W per workgroup for N output rows: spread N over 256 workgroups (one
+// per compute unit), a multiple of 4, at most 32 (two 16-row MFMA tiles).
 __host__ __device__ inline int gemm_rows_per_wg(int N) {
   int r = (N + 255) / 256;
   r = (r + 3) & ~3;
   if (r < 4) r = 4;
   if (r > 32) r = 32;
   return r;
+}
+
+// The epilogue of quad q: rows r .. r+3 of token m, stored as two bf16 pairs;
+// the row count of a workgroup is even, so each pair is all-in or all-out.
+__device__ __forceinline__ void store_quad_pairs(uint16_t* row, int r, int rows, u32x2 v) {
+  if (r < rows) *reinterpret_cast<unsigned*>(row + r) = v.x;
+  if (r + 2 < rows) *reinterpret_cast<unsigned*>(row + r + 2) = v.y;
 }
 
 }  // namespace attnres

@@ -22,7 +22,7 @@ __global__ __launch_bounds__(NW * 64) void wsgemm_kernel(GemmParams p, int R) {
     if (m < p.M && r < rows) {
       const f32x4 s = C::gather(red, q);
       const u32x2 v = {positive_zero(pack2(s.x, s.y)), positive_zero(pack2(s.z, s.w))};
-      st8(p.y + (size_t)m * p.ldy + row0 + r, v);
+      store_quad_pairs(p.y + (size_t)m * p.ldy + row0, r, rows, v);
     }
   }
 }
@@ -30,7 +30,7 @@ __global__ __launch_bounds__(NW * 64) void wsgemm_kernel(GemmParams p, int R) {
 template <int RT, int TT>
 static hipError_t go(const GemmParams& p, int R, hipStream_t stream) {
   constexpr int NW = 8;
-  constexpr int D = TT == 1 ? 8 : TT == 2 ? 6 : 4;
+  constexpr int D = TT == 1 ? 8 : TT == 2 ? 6 : TT == 3 ? 4 : 3;
   const int grid = (p.N + R - 1) / R;
   hipLaunchKernelGGL((wsgemm_kernel<RT, TT, NW, D>), dim3(grid), dim3(NW * 64), 0, stream, p, R);
   return hipGetLastError();

@@ -28,6 +28,7 @@ def lib():
                                     I64, F, F, I, I, I, I, I, I, P, SZ, P]
     L.attnres_oproj_workspace_size.argtypes = [I, I, I]
     L.attnres_oproj_workspace_size.restype = SZ
+    L.attnres_oproj_workspace_init.argtypes = [P, SZ, P]
     L.attnres_strerror.argtypes = [I]
     L.attnres_strerror.restype = ctypes.c_char_p
     return L
@@ -41,7 +42,7 @@ def declared_functions():
 def test_header_symbols_exported(lib):
     names = declared_functions()
     assert set(names) == {"attnres_run", "wsgemm_run", "attnres_oproj_workspace_size",
-                          "attnres_oproj_run", "attnres_strerror"}
+                          "attnres_oproj_workspace_init", "attnres_oproj_run", "attnres_strerror"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -59,7 +60,13 @@ def test_strerror_and_workspace(lib):
     for c, word in codes.items():
         assert word in lib.attnres_strerror(c)
     assert b"unknown" in lib.attnres_strerror(-99)
-    assert lib.attnres_oproj_workspace_size(64, 7168, 8) >= 8
+    assert lib.attnres_oproj_workspace_size(64, 7168, 8) == 256 + 64 * 7168 * 2
+    assert lib.attnres_oproj_workspace_size(1, 8, 0) == 512
+    # host-side rejections of the init call (no launch happens)
+    assert lib.attnres_oproj_workspace_init(None, 1024, None) == -5
+    assert lib.attnres_oproj_workspace_init(A + 16, 1024, None) == -5
+    assert lib.attnres_oproj_workspace_init(A, 128, None) == -5
+    assert lib.attnres_oproj_workspace_init(A, 1026, None) == -5
 
 
 # Fake, 256-byte-aligned addresses: validation only looks at their values.
@@ -121,7 +128,7 @@ def test_wsgemm_run_empty_is_a_noop(lib):
 
 def call_fused(lib, **kw):
     a = attn_args()
-    a.update(x=A, ldx=8192, W=A, ldw=8192, K=8192, ws=A, wsb=256, M=4)
+    a.update(x=A, ldx=8192, W=A, ldw=8192, K=8192, ws=A, wsb=256 + 4 * 7168 * 2, M=4)
     a.update(kw)
     return lib.attnres_oproj_run(a["x"], a["ldx"], a["W"], a["ldw"], a["K"], a["prefix"],
                                  a["ld_prefix"], a["blocks"], a["bst_t"], a["bst_b"], a["cap"],
@@ -133,7 +140,7 @@ def call_fused(lib, **kw):
 
 @pytest.mark.parametrize("change,code", [
     (dict(x=None), -1), (dict(W=None), -1), (dict(M=0), -3), (dict(M=65), -3), (dict(K=8190), -4),
-    (dict(ldx=4096), -1), (dict(W=A + 8), -2), (dict(ws=None), -5), (dict(wsb=8), -5),
+    (dict(ldx=4096), -1), (dict(W=A + 8), -2), (dict(ws=None), -5), (dict(wsb=8), -5), (dict(wsb=256 + 4 * 7168 * 2 - 2), -5),
     (dict(ws=A + 16), -5), (dict(nb=9, cap=10, bst_t=10 * H), -3), (dict(H=100), -4),
 ])
 def test_attnres_oproj_run_rejects(lib, change, code):
