@@ -37,10 +37,6 @@ namespace attnres {
 
 constexpr int kMaxTokensPerOwner = 4;
 
-#ifndef FUSED_D
-#define FUSED_D(TT) ((TT) == 1 ? 8 : (TT) == 2 ? 6 : (TT) == 3 ? 4 : 3)
-#endif
-
 __device__ __forceinline__ void st4_device(void* p, unsigned v) {
   __hip_atomic_store(reinterpret_cast<unsigned*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -66,16 +62,19 @@ __device__ __forceinline__ u32x4 collect_chunk(const unsigned* p, FusedWorkspace
   return u32x4{lo.x, lo.y, hi.x, hi.y};
 }
 
-template <int RT, int TT, int D>
+template <int RT, int TT>
 __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int R, int G, int NO) {
   constexpr int NT = kTokenThreads, NW = NT / 64;
-  using C = GemmCore<RT, TT, NW, D>;
+  using C = GemmLdsFor<RT, TT>;
+  static_assert(C::NT == NT, "one workgroup shape for both roles");
+  static_assert(NW * C::kQuads * sizeof(f32x4) <= C::kLdsBytes, "partials fit the ring");
   constexpr int NCH = TokenShape<NT>::NCH;
   union Smem {
-    f32x4 red[NW * C::kQuads];
+    char ring[C::kLdsBytes];  // GEMM role: chunk ring, then the K partials
     float mix[kMaxTokensPerOwner][kMaxH];
   };
-  __shared__ Smem sm;
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  f32x4* red = reinterpret_cast<f32x4*>(sm.ring);
   __shared__ float lds_pre[NW * 16], lds_post[NW * 4], lds_fin[NW];
 
   const AttnParams& a = f.a;
@@ -100,13 +99,13 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
     }
     {
       C core;
-      core.start(f.x, f.ldx, f.W, f.ldw, M, f.K, row0, rows);
+      core.start(f.x, f.ldx, f.W, f.ldw, M, f.K, row0, rows, sm.ring);
       core.finish();
-      core.stash(sm.red);
+      core.stash(red);
     }
     __syncthreads();
     if (qvalid) {
-      const f32x4 s = C::gather(sm.red, tid);
+      const f32x4 s = C::gather(red, tid);
       const unsigned y01 = positive_zero(pack2(s.x, s.y)), y23 = positive_zero(pack2(s.z, s.w));
       u32x2 nv;
       if (a.has_delta) {
@@ -229,8 +228,7 @@ int compute_units() {
 
 template <int RT, int TT>
 hipError_t go(const FusedParams& p, int R, int G, int NO, hipStream_t stream) {
-  constexpr int D = FUSED_D(TT);
-  hipLaunchKernelGGL((fused_kernel<RT, TT, D>), dim3(G + NO), dim3(kTokenThreads), 0, stream, p, R, G,
+  hipLaunchKernelGGL((fused_kernel<RT, TT>), dim3(G + NO), dim3(kTokenThreads), 0, stream, p, R, G,
                      NO);
   return hipGetLastError();
 }

@@ -139,6 +139,213 @@ struct GemmCore {
   }
 };
 
+// ---- LDS-staged core ---------------------------------------------------------
+//
+// The same product with W and x staged through LDS by direct global->LDS
+// loads (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l, no
+// VGPR involved), so the bytes a compute unit keeps in flight are bounded by
+// LDS, not by registers, and every load instruction reads whole row segments
+// (KCB contiguous bytes per row) instead of 64-byte MFMA fragments.
+//
+//   * K is cut into chunks of KE = KCB / 2 elements. A chunk holds, for the
+//     workgroup's R rows of W and the M rows of x, KCB bytes per row; a ring
+//     of NSLOT chunk slots keeps NSLOT - 1 chunks in flight while one is
+//     consumed. All NW wavefronts load parts of every chunk (one instruction
+//     per 1 KiB: 1024 / KCB rows) and consume it: wavefront w takes the
+//     k-steps [w SPW, (w + 1) SPW) of each chunk, so a wavefront's partial sum
+//     still runs in K order and the NW partials are added in wavefront order.
+//   * Inside a row the 16-byte pieces are stored XOR-swizzled by (row & 15):
+//     piece p of LDS row r sits at position p ^ (r & 15). An MFMA fragment
+//     read (16 rows, one piece each) then touches 16 distinct bank groups.
+//   * Rows past R, tokens past M and pieces past K are never loaded. Stale LDS
+//     in rows past R or tokens past M only reaches output rows / tokens that
+//     are discarded (MFMA output elements are independent); k-steps that
+//     straddle K are masked to zero in registers.
+//   * One workgroup barrier per chunk: after it, chunk c is complete (each
+//     wavefront waited for its own loads of c) and every wavefront has
+//     finished reading chunk c - 1, whose slot is refilled next.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);  // vmcnt(N) lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// vmcnt(n) lgkmcnt(0) for a wave-uniform 0 <= n <= N (waitcnt immediates
+// exist only at compile time, hence the chain).
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+  if constexpr (N == 0) {
+    wait_vmem_n<0>();
+  } else {
+    if (n >= N) wait_vmem_n<N>();
+    else wait_vmem_upto<N - 1>(n);
+  }
+}
+
+// Workgroup barrier without a memory fence (the waits above are explicit).
+__device__ __forceinline__ void wg_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Cache-policy operand of global_load_lds: the non-temporal bit.
+constexpr int kCacheNT = 2;
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+template <int RT, int TT, int KCB, int NSLOT>
+struct GemmLds {
+  static constexpr int NW = 8, NT = NW * 64;
+  static constexpr int kQuads = RT * TT * 64;
+  static constexpr int WROWS = RT * 16, ROWS = WROWS + TT * 16;
+  static constexpr int SLOT = ROWS * KCB;
+  static constexpr int kLdsBytes = NSLOT * SLOT;
+  static constexpr int KE = KCB / 2;       // k per chunk
+  static constexpr int STEPS = KE / 32;    // 32-wide k-steps per chunk
+  static constexpr int SPW = STEPS / NW;   // k-steps per wavefront per chunk
+  static constexpr int PIECES = KCB / 16;  // 16-byte pieces per row segment
+  static constexpr int RPI = 1024 / KCB;   // rows per load instruction
+  static constexpr int MAXSEG = ((WROWS + TT * 16) / RPI + NW - 1) / NW;
+  static_assert(STEPS % NW == 0 && SPW >= 1, "a chunk must give every wavefront k-steps");
+  static_assert(PIECES >= 16 && KCB <= 1024, "swizzle needs at least 16 pieces per row");
+  static_assert(NSLOT >= 2, "ring");
+
+  lds_char* ring;           // kLdsBytes of LDS
+  const char* gp[MAXSEG];   // this lane's source for chunk 0 of each of its segments
+  uint32_t dst[MAXSEG];     // segment offset inside a slot (wave-uniform)
+  uint32_t kb[MAXSEG];      // byte offset of this lane's piece inside a chunk
+  bool rv[MAXSEG];          // this lane's row exists
+  int nseg, nwseg, nC, K, wave, r16, kq;
+  f32x4 acc[RT][TT];
+
+  __device__ __forceinline__ void issue(int c) {
+    const uint32_t cb = (uint32_t)c * KCB;
+    lds_char* slot = ring + (c % NSLOT) * SLOT;
+#pragma unroll
+    for (int i = 0; i < MAXSEG; ++i) {
+      if (i < nseg) {
+        if (rv[i] && cb + kb[i] < (uint32_t)(2 * K)) {
+          if (i < nwseg)  // W is read once: non-temporal
+            __builtin_amdgcn_global_load_lds(gp[i] + cb, slot + dst[i], 16, 0, kCacheNT);
+          else
+            __builtin_amdgcn_global_load_lds(gp[i] + cb, slot + dst[i], 16, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Sets up this wavefront's segments and issues the first NSLOT - 1 chunks.
+  __device__ __forceinline__ void start(const uint16_t* __restrict__ x, int64_t ldx,
+                                        const uint16_t* __restrict__ W, int64_t ldw, int M,
+                                        int K_, int row0, int rows, char* lds) {
+    const int lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    r16 = lane & 15;
+    kq = lane >> 4;
+    K = K_;
+    ring = (lds_char*)lds;
+    nC = (K + KE - 1) / KE;
+    const int wseg = (rows + RPI - 1) / RPI, xseg = (M + RPI - 1) / RPI;
+    const int S = wseg + xseg;
+    nseg = wave < S ? (S - wave + NW - 1) / NW : 0;
+    nwseg = wave < wseg ? (wseg - wave + NW - 1) / NW : 0;  // W segments come first
+    const int lr = lane / PIECES, q = lane % PIECES;
+#pragma unroll
+    for (int i = 0; i < MAXSEG; ++i) {
+      const int sidx = wave + i * NW;
+      const bool isw = sidx < wseg;
+      const int r = (isw ? sidx : sidx - wseg) * RPI + lr;  // row within W rows or x rows
+      const int lrow = (isw ? 0 : WROWS) + r;                // LDS row
+      const int p = q ^ (lrow & 15);
+      rv[i] = isw ? r < rows : r < M;
+      const int rr = rv[i] ? r : 0;
+      gp[i] = isw ? reinterpret_cast<const char*>(W + (size_t)(row0 + rr) * ldw) + 16 * p
+                  : reinterpret_cast<const char*>(x + (size_t)rr * ldx) + 16 * p;
+      kb[i] = 16 * p;
+      dst[i] = __builtin_amdgcn_readfirstlane(((isw ? 0 : WROWS) + (sidx < wseg ? sidx : sidx - wseg) * RPI) * KCB);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = 0; c < NSLOT - 1 && c < nC; ++c) issue(c);
+  }
+
+  __device__ __forceinline__ void compute(int c) {
+    const lds_char* slot = ring + (c % NSLOT) * SLOT;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int ks = wave * SPW + j;
+      const int k0 = c * KE + ks * 32;
+      if (k0 < K) {
+        const int off = 16 * ((ks * 4 + kq) ^ r16);
+        u32x4 a[RT], b[TT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          a[rt] = *reinterpret_cast<const lds_u32x4*>(slot + (rt * 16 + r16) * KCB + off);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+          b[tt] = *reinterpret_cast<const lds_u32x4*>(slot + (WROWS + tt * 16 + r16) * KCB + off);
+        if (k0 + 32 > K && k0 + 8 * kq >= K) {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) a[rt] = zero;
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) b[tt] = zero;
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = mfma_bf16(a[rt], b[tt], acc[rt][tt]);
+      }
+    }
+  }
+
+  // Consumes every chunk; returns with all loads complete and all wavefronts
+  // past their last LDS read of the ring.
+  __device__ __forceinline__ void finish() {
+    for (int c = 0; c < nC; ++c) {
+      const int ahead = min(c + NSLOT - 2, nC - 1) - c;  // chunks after c already issued
+      wait_vmem_upto<MAXSEG * (NSLOT - 2)>(nseg * ahead);
+      wg_barrier();
+      if (c + NSLOT - 1 < nC) issue(c + NSLOT - 1);
+      compute(c);
+    }
+    wait_vmem_n<0>();
+    wg_barrier();
+  }
+
+  __device__ __forceinline__ void stash(f32x4* red) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) red[((wave * RT + rt) * TT + tt) * 64 + lane] = acc[rt][tt];
+  }
+
+  __device__ static __forceinline__ f32x4 gather(const f32x4* red, int q) {
+    f32x4 s = red[q];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) s += red[w * kQuads + q];
+    return s;
+  }
+
+  __device__ static __forceinline__ void quad_coords(int q, int& m, int& r) {
+    const int rt = q / (TT * 64), tt = (q / 64) % TT, ln = q & 63;
+    m = tt * 16 + (ln & 15);
+    r = rt * 16 + 4 * (ln >> 4);
+  }
+};
+
+// Chunk shape per token-tile count: 1 KiB row segments and three slots for
+// up to 16 tokens; 512-byte segments beyond (x then dominates a chunk).
+template <int RT, int TT>
+using GemmLdsFor = GemmLds<RT, TT, (TT == 1 ? 1024 : 512), (TT == 1 ? 3 : TT == 2 ? 4 : 3)>;
+
 // Rows of W per workgroup for N output rows: spread N over 256 workgroups (one
 // per compute unit), a multiple of 4, at most 32 (two 16-row MFMA tiles).
 __host__ __device__ inline int gemm_rows_per_wg(int N) {

@@ -5,14 +5,17 @@
 
 namespace attnres {
 
-template <int RT, int TT, int NW, int D>
-__global__ __launch_bounds__(NW * 64) void wsgemm_kernel(GemmParams p, int R) {
-  using C = GemmCore<RT, TT, NW, D>;
-  __shared__ f32x4 red[NW * C::kQuads];
+template <int RT, int TT>
+__global__ __launch_bounds__(512) void wsgemm_kernel(GemmParams p, int R) {
+  using C = GemmLdsFor<RT, TT>;
+  static_assert(C::NT == 512, "launch bounds");
+  static_assert(C::NW * C::kQuads * sizeof(f32x4) <= C::kLdsBytes, "partials fit the ring");
+  __shared__ __attribute__((aligned(16))) char lds[C::kLdsBytes];
+  f32x4* red = reinterpret_cast<f32x4*>(lds);  // reused once the ring is drained
   const int row0 = blockIdx.x * R;
   const int rows = min(R, p.N - row0);
   C core;
-  core.start(p.x, p.ldx, p.W, p.ldw, p.M, p.K, row0, rows);
+  core.start(p.x, p.ldx, p.W, p.ldw, p.M, p.K, row0, rows, lds);
   core.finish();
   core.stash(red);
   __syncthreads();
@@ -29,10 +32,8 @@ __global__ __launch_bounds__(NW * 64) void wsgemm_kernel(GemmParams p, int R) {
 
 template <int RT, int TT>
 static hipError_t go(const GemmParams& p, int R, hipStream_t stream) {
-  constexpr int NW = 8;
-  constexpr int D = TT == 1 ? 8 : TT == 2 ? 6 : TT == 3 ? 4 : 3;
   const int grid = (p.N + R - 1) / R;
-  hipLaunchKernelGGL((wsgemm_kernel<RT, TT, NW, D>), dim3(grid), dim3(NW * 64), 0, stream, p, R);
+  hipLaunchKernelGGL((wsgemm_kernel<RT, TT>), dim3(grid), dim3(GemmLdsFor<RT, TT>::NT), 0, stream, p, R);
   return hipGetLastError();
 }
 

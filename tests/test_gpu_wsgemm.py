@@ -53,7 +53,8 @@ def test_wsgemm_config4(M):
 
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 7168), (8, 7168, 1024), (13, 1000, 1000),
                                    (16, 4096, 7168), (33, 264, 520), (64, 7168, 4096),
-                                   (64, 8, 8), (5, 16384, 64)])
+                                   (64, 8, 8), (5, 16384, 64), (17, 96, 1016), (49, 520, 24),
+                                   (2, 7168, 1032), (31, 40, 8200)])
 def test_wsgemm_exact_integers(M, N, K):
     xi = rng.integers(-8, 9, (M, K))
     wi = rng.integers(-8, 9, (N, K))
