@@ -116,6 +116,16 @@ __device__ __forceinline__ void wait_vmem() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Workgroup barrier for LDS traffic: waits for this wavefront's LDS operations
+// (lgkmcnt(0)) but not for its global stores, which __syncthreads() would
+// also drain (vmcnt(0)). Call from uniform control flow.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt and expcnt: no wait; lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---- fixed-order reductions --------------------------------------------------
 
 template <int CTRL>
@@ -127,20 +137,33 @@ __device__ __forceinline__ float readlane(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// Sum over the 64 lanes of a wavefront, in a fixed tree: butterflies inside
-// each 16-lane row (xor 1, xor 2, half-row mirror, row mirror; the two addends
-// of every pair are the same numbers, so all lanes of a row agree bit for bit),
-// then ((row0 + row1) + (row2 + row3)). Must be called with all lanes active.
-__device__ __forceinline__ float wave_sum(float v) {
+// DPP move with a row mask: rows outside `ROW_MASK` read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_rows(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wavefront, in a fixed tree, left in lane 63:
+// butterflies inside each 16-lane row (xor 1, xor 2, half-row mirror, row
+// mirror; the two addends of every pair are the same numbers, so all lanes of
+// a row agree bit for bit), then row_bcast:15 (row 1 += row 0, row 3 += row 2)
+// and row_bcast:31 (row 3 += lane 31): lane 63 holds
+// (row0 + row1) + (row2 + row3). Must be called with all lanes active.
+__device__ __forceinline__ float wave_sum63(float v) {
   v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
   v += dpp<0x141>(v);  // row_half_mirror
   v += dpp<0x140>(v);  // row_mirror
-  return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
+  v += dpp_rows<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_rows<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
 }
 
+// The same sum, returned to every lane.
+__device__ __forceinline__ float wave_sum(float v) { return readlane(wave_sum63(v), 63); }
+
 // Sums K per-thread partials over a workgroup of NW wavefronts: wavefront sums
-// (wave_sum), then the NW wavefront totals in wavefront order. Every thread
+// (wave_sum63), then the NW wavefront totals in wavefront order. Every thread
 // gets the totals in v. `lds` holds NW*K floats and must not be reused by
 // another reduction of the same workgroup until all threads have returned.
 // Contains a workgroup barrier: call from uniform control flow.
@@ -149,12 +172,12 @@ __device__ __forceinline__ void wg_sum(float (&v)[K], float* lds) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float t[K];
 #pragma unroll
-  for (int k = 0; k < K; ++k) t[k] = wave_sum(v[k]);
-  if (lane == 0) {
+  for (int k = 0; k < K; ++k) t[k] = wave_sum63(v[k]);
+  if (lane == 63) {
 #pragma unroll
     for (int k = 0; k < K; ++k) lds[wave * K + k] = t[k];
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     float s = lds[k];

@@ -41,25 +41,74 @@ __device__ __forceinline__ void st4_device(void* p, unsigned v) {
   __hip_atomic_store(reinterpret_cast<unsigned*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Polls one 8-column chunk (four words) of a mailbox row until no word holds
-// the sentinel; gives up after kSpinLimit rounds (about a second), flagging
-// the workspace, so every wave terminates.
+// Collects this thread's chunks (four mailbox words each) of the owner's
+// tokens. Each round issues one 16-byte device-scope (sc1) buffer load per
+// chunk, all back to back; a chunk that has already arrived gets an offset
+// past the end of the buffer, which the hardware answers with zeros and no
+// memory access. A chunk is complete when none of its words holds the
+// sentinel. Gives up after kSpinLimit rounds (about a second), flagging the
+// workspace, so every wave terminates.
 constexpr int kSpinLimit = 1 << 20;
-__device__ __forceinline__ u32x4 collect_chunk(const unsigned* p, FusedWorkspace* ws) {
-  u32x2 lo, hi;
-  for (int spin = 0;; ++spin) {
-    lo = ld8_device(p);
-    hi = ld8_device(p + 2);
-    if (lo.x != kMailboxSentinel && lo.y != kMailboxSentinel && hi.x != kMailboxSentinel &&
-        hi.y != kMailboxSentinel)
-      break;
+constexpr unsigned kBufferOff = 0xFFFFFFF0u;  // past num_records: reads zeros
+constexpr int kBufferDword3 = 0x00020000;     // raw buffer, 32-bit data format
+constexpr int kCacheSC1 = 16;                 // buffer-load cache policy: device scope
+
+template <int KT, int NCH>
+__device__ __forceinline__ void collect(__amdgpu_buffer_rsrc_t mbox, const int (&tok)[KT], int ntok,
+                                        int H, u32x4 (&v)[KT][NCH], FusedWorkspace* ws) {
+  static_assert(KT * NCH <= 32, "pending mask");
+  const int tid = threadIdx.x, CH = H >> 3;
+  unsigned pending = 0;
+  unsigned off[KT][NCH];
+#pragma unroll
+  for (int k = 0; k < KT; ++k)
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = tid + j * kTokenThreads;
+      v[k][j] = u32x4{0u, 0u, 0u, 0u};
+      off[k][j] = (unsigned)tok[k] * (unsigned)(2 * H) + 16u * (unsigned)c;
+      if (k < ntok && c < CH) pending |= 1u << (k * NCH + j);
+    }
+  for (int spin = 0; pending != 0; ++spin) {
+    u32x4 r[KT][NCH];
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const bool p = pending & (1u << (k * NCH + j));
+        r[k][j] = __builtin_amdgcn_raw_buffer_load_b128(mbox, p ? off[k][j] : kBufferOff, 0, kCacheSC1);
+      }
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const unsigned bit = 1u << (k * NCH + j);
+        const u32x4 w = r[k][j];
+        if ((pending & bit) && w.x != kMailboxSentinel && w.y != kMailboxSentinel &&
+            w.z != kMailboxSentinel && w.w != kMailboxSentinel) {
+          v[k][j] = w;
+          pending &= ~bit;
+        }
+      }
+    if (pending == 0) break;
     if (spin >= kSpinLimit) {
       __hip_atomic_store(&ws->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
     __builtin_amdgcn_s_sleep(2);
   }
-  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+__device__ __forceinline__ void load_mix(const float* row, int c, bool valid, float (&m)[8]) {
+  if (valid) {
+    const f32x4* pm = reinterpret_cast<const f32x4*>(row + c * 8);
+    const f32x4 m0 = pm[0], m1 = pm[1];
+    m[0] = m0.x; m[1] = m0.y; m[2] = m0.z; m[3] = m0.w;
+    m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[i] = 0.0f;
+  }
 }
 
 template <int RT, int TT>
@@ -67,15 +116,17 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
   constexpr int NT = kTokenThreads, NW = NT / 64;
   using C = GemmLdsFor<RT, TT>;
   static_assert(C::NT == NT, "one workgroup shape for both roles");
+  // tokens per owner: one up to 16 tokens, at most four beyond
+  constexpr int KT = TT == 1 ? 1 : kMaxTokensPerOwner;
   static_assert(NW * C::kQuads * sizeof(f32x4) <= C::kLdsBytes, "partials fit the ring");
   constexpr int NCH = TokenShape<NT>::NCH;
   union Smem {
     char ring[C::kLdsBytes];  // GEMM role: chunk ring, then the K partials
-    float mix[kMaxTokensPerOwner][kMaxH];
+    float mix[KT][kMaxH];
   };
   __shared__ __attribute__((aligned(16))) Smem sm;
   f32x4* red = reinterpret_cast<f32x4*>(sm.ring);
-  __shared__ float lds_pre[NW * 16], lds_post[NW * 4], lds_fin[NW];
+  __shared__ float lds_pre[NW * (4 * KT > 16 ? 4 * KT : 16)], lds_fin[NW];
 
   const AttnParams& a = f.a;
   const int g = blockIdx.x, tid = threadIdx.x, CH = a.H >> 3;
@@ -103,7 +154,7 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
       core.finish();
       core.stash(red);
     }
-    __syncthreads();
+    lds_barrier();
     if (qvalid) {
       const f32x4 s = C::gather(red, tid);
       const unsigned y01 = positive_zero(pack2(s.x, s.y)), y23 = positive_zero(pack2(s.z, s.w));
@@ -128,15 +179,15 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
   const int o = g - G;
   int ntok = 0;
 #pragma unroll
-  for (int k = 0; k < kMaxTokensPerOwner; ++k)
+  for (int k = 0; k < KT; ++k)
     if (o + k * NO < M) ntok = k + 1;
 
   u32x4 gq[NCH];
   float w[NCH][8];
   token_weights<NT, NCH>(a, w, gq);
-  PreScalars pre[kMaxTokensPerOwner];
+  PreScalars pre[KT];
 #pragma unroll
-  for (int k = 0; k < kMaxTokensPerOwner; ++k) {
+  for (int k = 0; k < KT; ++k) {
     pre[k] = PreScalars{0.0f, 0.0f};
     if (k < ntok) {
       float mix[NCH][8];
@@ -150,48 +201,65 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
           pm[1] = f32x4{mix[j][4], mix[j][5], mix[j][6], mix[j][7]};
         }
       }
-      __syncthreads();  // lds_pre is reused by the next token
+      lds_barrier();  // lds_pre is reused by the next token
     }
   }
 
+  // post: collect every token's new prefix, re-arm the mailbox words, then one
+  // batched reduction of the four post sums of all tokens
+  int tok[KT];
 #pragma unroll
-  for (int k = 0; k < kMaxTokensPerOwner; ++k) {
+  for (int k = 0; k < KT; ++k) tok[k] = k < ntok ? o + k * NO : o;
+  const __amdgpu_buffer_rsrc_t mbox =
+      __builtin_amdgcn_make_buffer_rsrc(f.mailbox, 0, M * a.H * 2, kBufferDword3);
+  u32x4 nbits[KT][NCH];
+  collect<KT, NCH>(mbox, tok, ntok, a.H, nbits, f.ws);
+  float pp[4 * KT];
+#pragma unroll
+  for (int k = 0; k < KT; ++k) {
+    pp[4 * k] = pp[4 * k + 1] = pp[4 * k + 2] = pp[4 * k + 3] = 0.0f;
     if (k < ntok) {
-      const int t = o + k * NO;
-      unsigned* box = f.mailbox + (size_t)t * (a.H >> 1);
-      u32x4 nbits[NCH];
-      float nw[NCH][8], mix[NCH][8];
+      float nw[NCH][8], mix[NCH][8], p4[4];
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int c = tid + j * NT;
         if (c < CH) {
-          nbits[j] = collect_chunk(box + c * 4, f.ws);
           // re-arm for the next call (device scope, like every mailbox access)
-          st8_device(box + c * 4, u32x2{kMailboxSentinel, kMailboxSentinel});
-          st8_device(box + c * 4 + 2, u32x2{kMailboxSentinel, kMailboxSentinel});
-          const f32x4* pm = reinterpret_cast<const f32x4*>(sm.mix[k] + c * 8);
-          const f32x4 m0 = pm[0], m1 = pm[1];
-          mix[j][0] = m0.x; mix[j][1] = m0.y; mix[j][2] = m0.z; mix[j][3] = m0.w;
-          mix[j][4] = m1.x; mix[j][5] = m1.y; mix[j][6] = m1.z; mix[j][7] = m1.w;
-        } else {
-          nbits[j] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) mix[j][i] = 0.0f;
+          unsigned* wbox = f.mailbox + (size_t)tok[k] * (a.H >> 1) + (size_t)c * 4;
+          st8_device(wbox, u32x2{kMailboxSentinel, kMailboxSentinel});
+          st8_device(wbox + 2, u32x2{kMailboxSentinel, kMailboxSentinel});
         }
-        unpack8(nbits[j], nw[j]);
+        load_mix(sm.mix[k], c, c < CH, mix[j]);
+        unpack8(nbits[k][j], nw[j]);
       }
-      float pp[4];
-      post_partials(nw, w, mix, pp);
-      wg_sum<4, NW>(pp, lds_post);
+      post_partials(nw, w, mix, p4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pp[4 * k + i] = p4[i];
+    }
+  }
+  wg_sum<4 * KT, NW>(pp, lds_pre);  // lds_pre is free: the last pre() ended with a barrier
+
+#pragma unroll
+  for (int k = 0; k < KT; ++k) {
+    if (k < ntok) {
+      const int t = o + k * NO;
+      float nw[NCH][8], mix[NCH][8];
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int c = tid + j * NT;
+        load_mix(sm.mix[k], c, c < CH, mix[j]);
+        unpack8(nbits[k][j], nw[j]);
+      }
       if (a.write >= 0 && a.write < a.nb) {  // a scored slot: written after pre() read it
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
           const int c = tid + j * NT;
-          if (c < CH) st16(a.blocks + t * a.bst_t + a.write * a.bst_b + (size_t)c * 8, nbits[j]);
+          if (c < CH) st16(a.blocks + t * a.bst_t + a.write * a.bst_b + (size_t)c * 8, nbits[k][j]);
         }
       }
-      finish_out<NT, NCH>(a, t, pre[k], pp, nw, mix, gq, lds_fin);
-      __syncthreads();  // lds_post / lds_fin are reused by the next token
+      const float tot[4] = {pp[4 * k], pp[4 * k + 1], pp[4 * k + 2], pp[4 * k + 3]};
+      finish_out<NT, NCH>(a, t, pre[k], tot, nw, mix, gq, lds_fin);
+      if (a.final_b) lds_barrier();  // lds_fin is reused by the next token
     }
   }
 }

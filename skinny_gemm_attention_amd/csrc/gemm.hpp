@@ -341,10 +341,13 @@ struct GemmLds {
   }
 };
 
-// Chunk shape per token-tile count: 1 KiB row segments and three slots for
-// up to 16 tokens; 512-byte segments beyond (x then dominates a chunk).
+// Chunk shape per tile shape (measured on MI355X): 512-byte row segments in
+// four slots for two row tiles and one token tile; 1 KiB segments in three
+// slots for a single row tile; 512-byte segments beyond 16 tokens, where x
+// dominates a chunk.
 template <int RT, int TT>
-using GemmLdsFor = GemmLds<RT, TT, (TT == 1 ? 1024 : 512), (TT == 1 ? 3 : TT == 2 ? 4 : 3)>;
+using GemmLdsFor = GemmLds<RT, TT, (TT == 1 && RT == 1 ? 1024 : 512),
+                           (TT == 1 ? (RT == 1 ? 3 : 4) : TT == 2 ? 4 : 3)>;
 
 // Rows of W per workgroup for N output rows: spread N over 256 workgroups (one
 // per compute unit), a multiple of 4, at most 32 (two 16-row MFMA tiles).

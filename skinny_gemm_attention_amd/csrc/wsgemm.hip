@@ -18,7 +18,7 @@ __global__ __launch_bounds__(512) void wsgemm_kernel(GemmParams p, int R) {
   core.start(p.x, p.ldx, p.W, p.ldw, p.M, p.K, row0, rows, lds);
   core.finish();
   core.stash(red);
-  __syncthreads();
+  lds_barrier();
   for (int q = threadIdx.x; q < C::kQuads; q += C::NT) {
     int m, r;
     C::quad_coords(q, m, r);
