@@ -87,7 +87,17 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
     }
   }
 
-  finish_out<NT, NCH>(a, t, pre, pp, nw, mix, g, lds_fin);
+  float gg[NCH][8], ng[NCH][8], mg[NCH][8];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    unpack8(g[j], gg[j]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ng[j][i] = nw[j][i] * gg[j][i];
+      mg[j][i] = mix[j][i] * gg[j][i];
+    }
+  }
+  finish_out<NT, NCH>(a, t, out_scalars(a, pre, pp), nw, ng, mix, mg, gg, lds_fin);
 }
 
 hipError_t launch_attnres(const AttnParams& p, hipStream_t stream) {

@@ -41,63 +41,15 @@ __device__ __forceinline__ void st4_device(void* p, unsigned v) {
   __hip_atomic_store(reinterpret_cast<unsigned*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Collects this thread's chunks (four mailbox words each) of the owner's
-// tokens. Each round issues one 16-byte device-scope (sc1) buffer load per
-// chunk, all back to back; a chunk that has already arrived gets an offset
-// past the end of the buffer, which the hardware answers with zeros and no
-// memory access. A chunk is complete when none of its words holds the
-// sentinel. Gives up after kSpinLimit rounds (about a second), flagging the
-// workspace, so every wave terminates.
+// Mailbox polling: one 16-byte device-scope (sc1) buffer load per pending
+// chunk per round, all issued back to back; a chunk that has already arrived
+// gets an offset past the end of the buffer, which the hardware answers with
+// zeros and no memory access. Every wait is bounded by kSpinLimit rounds
+// (about a second); an owner that gives up flags the workspace and finishes.
 constexpr int kSpinLimit = 1 << 20;
 constexpr unsigned kBufferOff = 0xFFFFFFF0u;  // past num_records: reads zeros
 constexpr int kBufferDword3 = 0x00020000;     // raw buffer, 32-bit data format
 constexpr int kCacheSC1 = 16;                 // buffer-load cache policy: device scope
-
-template <int KT, int NCH>
-__device__ __forceinline__ void collect(__amdgpu_buffer_rsrc_t mbox, const int (&tok)[KT], int ntok,
-                                        int H, u32x4 (&v)[KT][NCH], FusedWorkspace* ws) {
-  static_assert(KT * NCH <= 32, "pending mask");
-  const int tid = threadIdx.x, CH = H >> 3;
-  unsigned pending = 0;
-  unsigned off[KT][NCH];
-#pragma unroll
-  for (int k = 0; k < KT; ++k)
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = tid + j * kTokenThreads;
-      v[k][j] = u32x4{0u, 0u, 0u, 0u};
-      off[k][j] = (unsigned)tok[k] * (unsigned)(2 * H) + 16u * (unsigned)c;
-      if (k < ntok && c < CH) pending |= 1u << (k * NCH + j);
-    }
-  for (int spin = 0; pending != 0; ++spin) {
-    u32x4 r[KT][NCH];
-#pragma unroll
-    for (int k = 0; k < KT; ++k)
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const bool p = pending & (1u << (k * NCH + j));
-        r[k][j] = __builtin_amdgcn_raw_buffer_load_b128(mbox, p ? off[k][j] : kBufferOff, 0, kCacheSC1);
-      }
-#pragma unroll
-    for (int k = 0; k < KT; ++k)
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const unsigned bit = 1u << (k * NCH + j);
-        const u32x4 w = r[k][j];
-        if ((pending & bit) && w.x != kMailboxSentinel && w.y != kMailboxSentinel &&
-            w.z != kMailboxSentinel && w.w != kMailboxSentinel) {
-          v[k][j] = w;
-          pending &= ~bit;
-        }
-      }
-    if (pending == 0) break;
-    if (spin >= kSpinLimit) {
-      __hip_atomic_store(&ws->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-}
 
 __device__ __forceinline__ void load_mix(const float* row, int c, bool valid, float (&m)[8]) {
   if (valid) {
@@ -120,9 +72,12 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
   constexpr int KT = TT == 1 ? 1 : kMaxTokensPerOwner;
   static_assert(NW * C::kQuads * sizeof(f32x4) <= C::kLdsBytes, "partials fit the ring");
   constexpr int NCH = TokenShape<NT>::NCH;
+  constexpr bool kOne = KT == 1;
   union Smem {
     char ring[C::kLdsBytes];  // GEMM role: chunk ring, then the K partials
-    float mix[KT][kMaxH];
+    struct {
+      float mix[kOne ? 1 : KT][kOne ? 1 : kMaxH];  // owner role, several tokens
+    } o;
   };
   __shared__ __attribute__((aligned(16))) Smem sm;
   f32x4* red = reinterpret_cast<f32x4*>(sm.ring);
@@ -182,10 +137,12 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
   for (int k = 0; k < KT; ++k)
     if (o + k * NO < M) ntok = k + 1;
 
-  u32x4 gq[NCH];
-  float w[NCH][8];
-  token_weights<NT, NCH>(a, w, gq);
+  float gg[NCH][8], w[NCH][8];
+  token_weights<NT, NCH>(a, w, gg);
   PreScalars pre[KT];
+  // one token: its mixture (and mixture*gains) stay in registers; more
+  // tokens park their mixtures in LDS
+  float mix1[kOne ? NCH : 1][8], mg1[kOne ? NCH : 1][8];
 #pragma unroll
   for (int k = 0; k < KT; ++k) {
     pre[k] = PreScalars{0.0f, 0.0f};
@@ -195,8 +152,14 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int c = tid + j * NT;
-        if (c < CH) {
-          f32x4* pm = reinterpret_cast<f32x4*>(sm.mix[k] + c * 8);
+        if (kOne) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            mix1[kOne ? j : 0][i] = mix[j][i];
+            mg1[kOne ? j : 0][i] = mix[j][i] * gg[j][i];
+          }
+        } else if (c < CH) {
+          f32x4* pm = reinterpret_cast<f32x4*>(sm.o.mix[k] + c * 8);
           pm[0] = f32x4{mix[j][0], mix[j][1], mix[j][2], mix[j][3]};
           pm[1] = f32x4{mix[j][4], mix[j][5], mix[j][6], mix[j][7]};
         }
@@ -205,50 +168,138 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
     }
   }
 
-  // post: collect every token's new prefix, re-arm the mailbox words, then one
-  // batched reduction of the four post sums of all tokens
+  // post: collect every token's new prefix from the mailbox. Each chunk's
+  // post partials (and, for one token, new*gains) are formed as soon as it
+  // arrives and its mailbox words are re-armed; only the reduction and the
+  // output remain once the last chunk is in.
   int tok[KT];
 #pragma unroll
   for (int k = 0; k < KT; ++k) tok[k] = k < ntok ? o + k * NO : o;
   const __amdgpu_buffer_rsrc_t mbox =
       __builtin_amdgcn_make_buffer_rsrc(f.mailbox, 0, M * a.H * 2, kBufferDword3);
   u32x4 nbits[KT][NCH];
-  collect<KT, NCH>(mbox, tok, ntok, a.H, nbits, f.ws);
-  float pp[4 * KT];
+  float pc[KT][NCH][4];
+  float ngo[kOne ? NCH : 1][8];  // new*gains of the one token
+  unsigned pending = 0, todo = 0;
 #pragma unroll
-  for (int k = 0; k < KT; ++k) {
-    pp[4 * k] = pp[4 * k + 1] = pp[4 * k + 2] = pp[4 * k + 3] = 0.0f;
-    if (k < ntok) {
-      float nw[NCH][8], mix[NCH][8], p4[4];
+  for (int k = 0; k < KT; ++k)
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      nbits[k][j] = u32x4{0u, 0u, 0u, 0u};
+      pc[k][j][0] = pc[k][j][1] = pc[k][j][2] = pc[k][j][3] = 0.0f;
+      if (k < ntok && tid + j * NT < CH) pending |= 1u << (k * NCH + j);
+    }
+#pragma unroll
+  for (int j = 0; j < (kOne ? NCH : 1); ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ngo[j][i] = 0.0f;
+  // a chunk that has arrived: form its partials (stores wait until the end:
+  // a wavefront's loads of the next round would wait for them too)
+  auto absorb = [&](unsigned& bits) {
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
-        const int c = tid + j * NT;
-        if (c < CH) {
-          // re-arm for the next call (device scope, like every mailbox access)
-          unsigned* wbox = f.mailbox + (size_t)tok[k] * (a.H >> 1) + (size_t)c * 4;
-          st8_device(wbox, u32x2{kMailboxSentinel, kMailboxSentinel});
-          st8_device(wbox + 2, u32x2{kMailboxSentinel, kMailboxSentinel});
-        }
-        load_mix(sm.mix[k], c, c < CH, mix[j]);
-        unpack8(nbits[k][j], nw[j]);
-      }
-      post_partials(nw, w, mix, p4);
+        const unsigned bit = 1u << (k * NCH + j);
+        if (bits & bit) {
+          const int c = tid + j * NT;
+          float nw[8], mx[8];
+          unpack8(nbits[k][j], nw);
+          if (kOne) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pp[4 * k + i] = p4[i];
+            for (int i = 0; i < 8; ++i) {
+              mx[i] = mix1[kOne ? j : 0][i];
+              ngo[kOne ? j : 0][i] = nw[i] * gg[j][i];
+            }
+          } else {
+            load_mix(sm.o.mix[k], c, true, mx);
+          }
+          chunk_post(nw, w[j], mx, pc[k][j]);
+        }
+      }
+    bits = 0;
+  };
+  for (int spin = 0; pending != 0; ++spin) {
+    u32x4 r[KT][NCH];
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const bool p = pending & (1u << (k * NCH + j));
+        const unsigned off = (unsigned)tok[k] * (unsigned)(2 * a.H) + 16u * (unsigned)(tid + j * NT);
+        r[k][j] = __builtin_amdgcn_raw_buffer_load_b128(mbox, p ? off : kBufferOff, 0, kCacheSC1);
+      }
+    absorb(todo);  // the previous round's arrivals, while these loads are in flight
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const unsigned bit = 1u << (k * NCH + j);
+        const u32x4 v = r[k][j];
+        if ((pending & bit) && v.x != kMailboxSentinel && v.y != kMailboxSentinel &&
+            v.z != kMailboxSentinel && v.w != kMailboxSentinel) {
+          pending &= ~bit;
+          todo |= bit;
+          nbits[k][j] = v;
+        }
+      }
+    if (pending == 0) break;
+    if (spin >= kSpinLimit) {
+      __hip_atomic_store(&f.ws->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
     }
+    __builtin_amdgcn_s_sleep(2);
   }
+  absorb(todo);
+  // re-arm the collected mailbox words for the next call (device scope, like
+  // every mailbox access); nothing below waits for these stores
+#pragma unroll
+  for (int k = 0; k < KT; ++k)
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = tid + j * NT;
+      if (k < ntok && c < CH) {
+        unsigned* wbox = f.mailbox + (size_t)tok[k] * (a.H >> 1) + (size_t)c * 4;
+        st8_device(wbox, u32x2{kMailboxSentinel, kMailboxSentinel});
+        st8_device(wbox + 2, u32x2{kMailboxSentinel, kMailboxSentinel});
+      }
+    }
+  float pp[4 * KT];
+#pragma unroll
+  for (int k = 0; k < KT; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float s4 = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) s4 += pc[k][j][i];  // chunk order, as post_partials
+      pp[4 * k + i] = s4;
+    }
   wg_sum<4 * KT, NW>(pp, lds_pre);  // lds_pre is free: the last pre() ended with a barrier
 
 #pragma unroll
   for (int k = 0; k < KT; ++k) {
     if (k < ntok) {
       const int t = o + k * NO;
-      float nw[NCH][8], mix[NCH][8];
+      float nw[NCH][8], ng[NCH][8], mix[NCH][8], mg[NCH][8];
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int c = tid + j * NT;
-        load_mix(sm.mix[k], c, c < CH, mix[j]);
         unpack8(nbits[k][j], nw[j]);
+        if (kOne) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            mix[j][i] = mix1[kOne ? j : 0][i];
+            mg[j][i] = mg1[kOne ? j : 0][i];
+            ng[j][i] = ngo[kOne ? j : 0][i];
+          }
+        } else {
+          load_mix(sm.o.mix[k], c, c < CH, mix[j]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            ng[j][i] = nw[j][i] * gg[j][i];
+            mg[j][i] = mix[j][i] * gg[j][i];
+          }
+        }
       }
       if (a.write >= 0 && a.write < a.nb) {  // a scored slot: written after pre() read it
 #pragma unroll
@@ -258,7 +309,7 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
         }
       }
       const float tot[4] = {pp[4 * k], pp[4 * k + 1], pp[4 * k + 2], pp[4 * k + 3]};
-      finish_out<NT, NCH>(a, t, pre[k], tot, nw, mix, gq, lds_fin);
+      finish_out<NT, NCH>(a, t, out_scalars(a, pre[k], tot), nw, ng, mix, mg, gg, lds_fin);
       if (a.final_b) lds_barrier();  // lds_fin is reused by the next token
     }
   }
