@@ -35,7 +35,7 @@
 
 namespace attnres {
 
-constexpr int kMaxTokensPerOwner = 4;
+constexpr int kMaxTokensPerOwner = 2;
 
 __device__ __forceinline__ void st4_device(void* p, unsigned v) {
   __hip_atomic_store(reinterpret_cast<unsigned*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -68,8 +68,8 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
   constexpr int NT = kTokenThreads, NW = NT / 64;
   using C = GemmLdsFor<RT, TT>;
   static_assert(C::NT == NT, "one workgroup shape for both roles");
-  // tokens per owner: one up to 16 tokens, at most four beyond
-  constexpr int KT = TT == 1 ? 1 : kMaxTokensPerOwner;
+  // tokens per owner: one up to 32 tokens, two beyond
+  constexpr int KT = TT <= 2 ? 1 : kMaxTokensPerOwner;
   static_assert(NW * C::kQuads * sizeof(f32x4) <= C::kLdsBytes, "partials fit the ring");
   constexpr int NCH = TokenShape<NT>::NCH;
   constexpr bool kOne = KT == 1;
@@ -356,8 +356,8 @@ hipError_t go(const FusedParams& p, int R, int G, int NO, hipStream_t stream) {
 
 hipError_t launch_fused(const FusedParams& p, hipStream_t stream) {
   const int H = p.a.H, M = p.a.T;
-  // owners: one token each up to 16 tokens, then up to four tokens each
-  const int per_owner = M <= 16 ? 1 : (M + 15) / 16;
+  // owners: one token each up to 32 tokens, then two tokens each
+  const int per_owner = M <= 32 ? 1 : kMaxTokensPerOwner;
   const int NO = (M + per_owner - 1) / per_owner;
   // GEMM rows per workgroup: even, at most 32, leaving NO compute units free
   int room = compute_units() - NO;
