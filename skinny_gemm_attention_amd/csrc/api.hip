@@ -77,11 +77,15 @@ AttnParams make_params(const void* delta, int64_t ld_delta, void* prefix, int64_
   return p;
 }
 
-// Header plus one bf16 mailbox row per token.
+// Header, one bf16 mailbox row per token, and (beyond 32 tokens) the split-K
+// hand-off.
+size_t mailbox_bytes(int M, int H) {
+  const size_t mailbox = (size_t)M * (size_t)H * 2;
+  return (mailbox + 255) & ~(size_t)255;
+}
 size_t workspace_bytes_for(int M, int H) {
   if (M < 0 || H < 0) return 0;
-  const size_t mailbox = (size_t)M * (size_t)H * 2;
-  return attnres::kWorkspaceHeader + ((mailbox + 255) & ~(size_t)255);
+  return attnres::kWorkspaceHeader + mailbox_bytes(M, H) + attnres::split_partial_bytes(M, H);
 }
 
 }  // namespace
@@ -176,6 +180,10 @@ int attnres_oproj_run(const void* x, int64_t ldx, const void* W, int64_t ldw, in
   p.K = K;
   p.ws = static_cast<attnres::FusedWorkspace*>(workspace);
   p.mailbox = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + attnres::kWorkspaceHeader);
+  p.partials = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
+                                           attnres::kWorkspaceHeader + mailbox_bytes(M, H));
+  p.ng = 0;
+  p.k_half = 0;
   return from_hip(attnres::launch_fused(p, static_cast<hipStream_t>(stream)));
 }
 

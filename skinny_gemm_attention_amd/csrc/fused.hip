@@ -63,14 +63,23 @@ __device__ __forceinline__ void load_mix(const float* row, int c, bool valid, fl
   }
 }
 
+template <bool SPLIT, int RT, int TT>
+struct FusedCore {
+  using type = GemmLdsFor<RT, TT>;
+};
 template <int RT, int TT>
+struct FusedCore<true, RT, TT> {
+  static_assert(RT * 16 == kSplitRows, "split-K row groups");
+  using type = GemmLdsSplit<TT>;
+};
+
+template <int RT, int TT, bool SPLIT>
 __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int R, int G, int NO) {
   constexpr int NT = kTokenThreads, NW = NT / 64;
-  using C = GemmLdsFor<RT, TT>;
+  using C = typename FusedCore<SPLIT, RT, TT>::type;
   static_assert(C::NT == NT, "one workgroup shape for both roles");
   // tokens per owner: one up to 32 tokens, two beyond
   constexpr int KT = TT <= 2 ? 1 : kMaxTokensPerOwner;
-  static_assert(NW * C::kQuads * sizeof(f32x4) <= C::kLdsBytes, "partials fit the ring");
   constexpr int NCH = TokenShape<NT>::NCH;
   constexpr bool kOne = KT == 1;
   union Smem {
@@ -89,43 +98,163 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
 
   if (g < G) {
     // ---- GEMM role: rows [row0, row0 + rows) for all M tokens -----------------------
-    const int row0 = g * R;
+    // Split K: workgroup g < ng streams the first K half of row group g and
+    // hands its FP32 partials to workgroup g + ng, which streams the second
+    // half, adds the two (first half first) and finishes the rows. The first
+    // half never waits; the second waits only on a lower workgroup id.
+    const bool second = SPLIT && g >= f.ng;
+    const int rg = SPLIT ? (second ? g - f.ng : g) : g;
+    const int row0 = rg * R;
     const int rows = min(R, a.H - row0);
-    int qm = 0, qr = 0;
-    bool qvalid = false;
-    u32x2 qprefix = {0u, 0u};
-    if (tid < C::kQuads) {
-      C::quad_coords(tid, qm, qr);
-      qvalid = qm < M && qr < rows;
-      if (qvalid && a.has_delta) {
-        const uint16_t* src = a.prefix + (size_t)qm * a.ld_prefix + row0 + qr;
-        qprefix.x = *reinterpret_cast<const unsigned*>(src);
-        if (qr + 2 < rows) qprefix.y = *reinterpret_cast<const unsigned*>(src + 2);
+    const int kbeg = second ? f.k_half : 0;
+    const int klen = SPLIT ? (second ? f.K - f.k_half : f.k_half) : f.K;
+    const bool finisher = !SPLIT || second;
+    constexpr int QPT = (C::kQuads + NT - 1) / NT;  // output quads per thread
+    // split finisher: thread (token tid / 8, rows 8 (tid % 8) .. + 7) writes
+    // the new prefix 16 bytes at a time
+    const int om = tid >> 3, oj = tid & 7;
+    const bool ov = SPLIT && second && om < M && 8 * oj < rows;
+    u32x4 oprefix = {0u, 0u, 0u, 0u};
+    if (ov && a.has_delta) oprefix = ld16(a.prefix + (size_t)om * a.ld_prefix + row0 + 8 * oj);
+    int qm[QPT], qr[QPT];
+    bool qv[QPT];
+    u32x2 qprefix[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int q = tid + i * NT;
+      qm[i] = qr[i] = 0;
+      qprefix[i] = u32x2{0u, 0u};
+      qv[i] = false;
+      if (q < C::kQuads) {
+        C::quad_coords(q, qm[i], qr[i]);
+        qv[i] = qm[i] < M && qr[i] < rows;
+        if (!SPLIT && qv[i] && a.has_delta) {
+          const uint16_t* src = a.prefix + (size_t)qm[i] * a.ld_prefix + row0 + qr[i];
+          qprefix[i].x = *reinterpret_cast<const unsigned*>(src);
+          if (qr[i] + 2 < rows) qprefix[i].y = *reinterpret_cast<const unsigned*>(src + 2);
+        }
       }
     }
     {
       C core;
-      core.start(f.x, f.ldx, f.W, f.ldw, M, f.K, row0, rows, sm.ring);
+      core.start(f.x, f.ldx, f.W, f.ldw, M, kbeg, klen, row0, rows, sm.ring);
       core.finish();
       core.stash(red);
     }
     lds_barrier();
-    if (qvalid) {
-      const f32x4 s = C::gather(red, tid);
-      const unsigned y01 = positive_zero(pack2(s.x, s.y)), y23 = positive_zero(pack2(s.z, s.w));
-      u32x2 nv;
-      if (a.has_delta) {
-        nv.x = pack2(add_round_odd(bf_lo(qprefix.x), bf_lo(y01)), add_round_odd(bf_hi(qprefix.x), bf_hi(y01)));
-        nv.y = pack2(add_round_odd(bf_lo(qprefix.y), bf_lo(y23)), add_round_odd(bf_hi(qprefix.y), bf_hi(y23)));
-      } else {
-        nv = u32x2{y01, y23};
+    f32x4 s[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) s[i] = qv[i] ? C::gather(red, tid + i * NT) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (SPLIT) {
+      const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
+          f.partials, 0, f.ng * C::kQuads * 16, kBufferDword3);
+      if (!second) {
+#pragma unroll
+        for (int i = 0; i < QPT; ++i) {
+          if (qv[i]) {  // +0.0 for a zero, so no stored word equals the sentinel
+            u32x4 v = __builtin_bit_cast(u32x4, s[i]);
+            v.x = v.x == kMailboxSentinel ? 0u : v.x;
+            v.y = v.y == kMailboxSentinel ? 0u : v.y;
+            v.z = v.z == kMailboxSentinel ? 0u : v.z;
+            v.w = v.w == kMailboxSentinel ? 0u : v.w;
+            __builtin_amdgcn_raw_buffer_store_b128(v, part, (rg * C::kQuads + tid + i * NT) * 16, 0,
+                                                   kCacheSC1);
+          }
+        }
+        return;
       }
-      unsigned* box = f.mailbox + (size_t)qm * (a.H >> 1) + ((row0 + qr) >> 1);
-      st4_device(box, nv.x);  // collected by token qm's owner
-      if (qr + 2 < rows) st4_device(box + 1, nv.y);
-      store_quad_pairs(a.prefix + (size_t)qm * a.ld_prefix + row0, qr, rows, nv);
-      if (a.aux) store_quad_pairs(a.aux + (size_t)qm * a.ld_aux + row0, qr, rows, nv);
-      if (a.write >= a.nb) store_quad_pairs(a.blocks + qm * a.bst_t + a.write * a.bst_b + row0, qr, rows, nv);
+      // the first half's partials: poll (as the owners poll the mailbox),
+      // add, re-arm
+      unsigned pending = 0;
+#pragma unroll
+      for (int i = 0; i < QPT; ++i)
+        if (qv[i]) pending |= 1u << i;
+      f32x4 first[QPT];
+      for (int spin = 0; pending != 0; ++spin) {
+        u32x4 r[QPT];
+#pragma unroll
+        for (int i = 0; i < QPT; ++i) {
+          const unsigned off = (unsigned)(rg * C::kQuads + tid + i * NT) * 16u;
+          r[i] = __builtin_amdgcn_raw_buffer_load_b128(part, (pending & (1u << i)) ? off : kBufferOff,
+                                                       0, kCacheSC1);
+        }
+#pragma unroll
+        for (int i = 0; i < QPT; ++i) {
+          const u32x4 v = r[i];
+          if ((pending & (1u << i)) && v.x != kMailboxSentinel && v.y != kMailboxSentinel &&
+              v.z != kMailboxSentinel && v.w != kMailboxSentinel) {
+            first[i] = __builtin_bit_cast(f32x4, v);
+            pending &= ~(1u << i);
+          }
+        }
+        if (pending == 0) break;
+        if (spin >= kSpinLimit) {
+          __hip_atomic_store(&f.ws->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int i = 0; i < QPT; ++i)
+            if (pending & (1u << i)) first[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      // y (rounded, -0.0 -> +0.0) of every quad into an LDS tile [token][64 rows]
+      unsigned* tile = reinterpret_cast<unsigned*>(sm.ring + C::NP * C::kQuads * 16);
+#pragma unroll
+      for (int i = 0; i < QPT; ++i) {
+        if (qv[i]) {
+          s[i] = first[i] + s[i];
+          const u32x4 sent = {kMailboxSentinel, kMailboxSentinel, kMailboxSentinel, kMailboxSentinel};
+          __builtin_amdgcn_raw_buffer_store_b128(sent, part, (rg * C::kQuads + tid + i * NT) * 16, 0,
+                                                 kCacheSC1);
+          unsigned* t2 = tile + qm[i] * (kSplitRows / 2) + (qr[i] >> 1);
+          t2[0] = positive_zero(pack2(s[i].x, s[i].y));
+          t2[1] = positive_zero(pack2(s[i].z, s[i].w));
+        }
+      }
+      lds_barrier();
+      if (ov) {
+        const u32x4 y = *reinterpret_cast<const u32x4*>(tile + om * (kSplitRows / 2) + 4 * oj);
+        u32x4 nv = y;
+        if (a.has_delta) {
+          float pf[8], yf[8], r[8];
+          unpack8(oprefix, pf);
+          unpack8(y, yf);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) r[e] = add_round_odd(pf[e], yf[e]);
+          nv = pack8(r);
+        }
+        const size_t col = (size_t)row0 + 8 * oj;
+        const __amdgpu_buffer_rsrc_t mb =
+            __builtin_amdgcn_make_buffer_rsrc(f.mailbox, 0, M * a.H * 2, kBufferDword3);
+        __builtin_amdgcn_raw_buffer_store_b128(nv, mb, (unsigned)((size_t)om * a.H + col) * 2u, 0,
+                                               kCacheSC1);  // collected by token om's owner
+        st16(a.prefix + (size_t)om * a.ld_prefix + col, nv);
+        if (a.aux) st16(a.aux + (size_t)om * a.ld_aux + col, nv);
+        if (a.write >= a.nb) st16(a.blocks + om * a.bst_t + a.write * a.bst_b + col, nv);
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      if (qv[i]) {
+        const unsigned y01 = positive_zero(pack2(s[i].x, s[i].y)), y23 = positive_zero(pack2(s[i].z, s[i].w));
+        u32x2 nv;
+        if (a.has_delta) {
+          nv.x = pack2(add_round_odd(bf_lo(qprefix[i].x), bf_lo(y01)),
+                       add_round_odd(bf_hi(qprefix[i].x), bf_hi(y01)));
+          nv.y = pack2(add_round_odd(bf_lo(qprefix[i].y), bf_lo(y23)),
+                       add_round_odd(bf_hi(qprefix[i].y), bf_hi(y23)));
+        } else {
+          nv = u32x2{y01, y23};
+        }
+        unsigned* box = f.mailbox + (size_t)qm[i] * (a.H >> 1) + ((row0 + qr[i]) >> 1);
+        st4_device(box, nv.x);  // collected by token qm's owner
+        if (qr[i] + 2 < rows) st4_device(box + 1, nv.y);
+        store_quad_pairs(a.prefix + (size_t)qm[i] * a.ld_prefix + row0, qr[i], rows, nv);
+        if (a.aux) store_quad_pairs(a.aux + (size_t)qm[i] * a.ld_aux + row0, qr[i], rows, nv);
+        if (a.write >= a.nb)
+          store_quad_pairs(a.blocks + qm[i] * a.bst_t + a.write * a.bst_b + row0, qr[i], rows, nv);
+      }
     }
     return;
   }
@@ -345,10 +474,10 @@ int compute_units() {
   return cached[dev];
 }
 
-template <int RT, int TT>
+template <int RT, int TT, bool SPLIT = false>
 hipError_t go(const FusedParams& p, int R, int G, int NO, hipStream_t stream) {
-  hipLaunchKernelGGL((fused_kernel<RT, TT>), dim3(G + NO), dim3(kTokenThreads), 0, stream, p, R, G,
-                     NO);
+  hipLaunchKernelGGL((fused_kernel<RT, TT, SPLIT>), dim3(G + NO), dim3(kTokenThreads), 0, stream, p,
+                     R, G, NO);
   return hipGetLastError();
 }
 
@@ -359,6 +488,20 @@ hipError_t launch_fused(const FusedParams& p, hipStream_t stream) {
   // owners: one token each up to 32 tokens, then two tokens each
   const int per_owner = M <= 32 ? 1 : kMaxTokensPerOwner;
   const int NO = (M + per_owner - 1) / per_owner;
+  const int tt = (M + 15) / 16;
+  // beyond 32 tokens: split K over pairs of workgroups with 64-row groups, when
+  // both halves and the owners fit the compute units
+  if (tt >= 3 && split_partial_bytes(M, H) > 0) {
+    const int ng = (H + kSplitRows - 1) / kSplitRows;
+    if (2 * ng + NO <= compute_units() && p.K >= 256) {
+      FusedParams q = p;
+      q.ng = ng;
+      q.k_half = ((p.K / 2 + 127) / 128) * 128;  // whole 256-byte chunks in the first half
+      if (q.k_half > p.K) q.k_half = p.K;
+      return tt == 3 ? go<4, 3, true>(q, kSplitRows, 2 * ng, NO, stream)
+                     : go<4, 4, true>(q, kSplitRows, 2 * ng, NO, stream);
+    }
+  }
   // GEMM rows per workgroup: even, at most 32, leaving NO compute units free
   int room = compute_units() - NO;
   if (room < 1) room = 1;
@@ -367,7 +510,6 @@ hipError_t launch_fused(const FusedParams& p, hipStream_t stream) {
   if (R < 2) R = 2;
   if (R > 32) R = 32;
   const int G = (H + R - 1) / R;
-  const int tt = (M + 15) / 16;
   if (R > 16) {
     switch (tt) {
       case 1: return go<2, 1>(p, R, G, NO, stream);

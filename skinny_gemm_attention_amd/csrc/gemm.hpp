@@ -151,9 +151,14 @@ struct GemmCore {
 //     workgroup's R rows of W and the M rows of x, KCB bytes per row; a ring
 //     of NSLOT chunk slots keeps NSLOT - 1 chunks in flight while one is
 //     consumed. All NW wavefronts load parts of every chunk (one instruction
-//     per 1 KiB: 1024 / KCB rows) and consume it: wavefront w takes the
-//     k-steps [w SPW, (w + 1) SPW) of each chunk, so a wavefront's partial sum
-//     still runs in K order and the NW partials are added in wavefront order.
+//     per 1 KiB: 1024 / KCB rows) and consume it. With at least NW k-steps per
+//     chunk, wavefront w takes the k-steps [w SPW, (w + 1) SPW) of each chunk
+//     for all row tiles; with fewer (STEPS < NW), wavefront w takes k-step
+//     w % STEPS for the row tiles of row group w / STEPS. Either way a
+//     wavefront's partial sums run in K order, and the NP partials of an
+//     output element are added in k-slice order.
+//   * The core streams a K range [k_begin, k_begin + K) of each row, so two
+//     workgroups can split K (the caller adds their partial products).
 //   * Inside a row the 16-byte pieces are stored XOR-swizzled by (row & 15):
 //     piece p of LDS row r sits at position p ^ (r & 15). An MFMA fragment
 //     read (16 rows, one piece each) then touches 16 distinct bank groups.
@@ -204,23 +209,27 @@ struct GemmLds {
   static constexpr int WROWS = RT * 16, ROWS = WROWS + TT * 16;
   static constexpr int SLOT = ROWS * KCB;
   static constexpr int kLdsBytes = NSLOT * SLOT;
-  static constexpr int KE = KCB / 2;       // k per chunk
-  static constexpr int STEPS = KE / 32;    // 32-wide k-steps per chunk
-  static constexpr int SPW = STEPS / NW;   // k-steps per wavefront per chunk
-  static constexpr int PIECES = KCB / 16;  // 16-byte pieces per row segment
-  static constexpr int RPI = 1024 / KCB;   // rows per load instruction
+  static constexpr int KE = KCB / 2;                 // k per chunk
+  static constexpr int STEPS = KE / 32;              // 32-wide k-steps per chunk
+  static constexpr int NP = STEPS < NW ? STEPS : NW; // k-partials per output element
+  static constexpr int RH = NW / NP;                 // row groups across wavefronts
+  static constexpr int SPW = STEPS / NP;             // k-steps per wavefront per chunk
+  static constexpr int RTW = RT / RH;                // row tiles per wavefront
+  static constexpr int PIECES = KCB / 16;            // 16-byte pieces per row segment
+  static constexpr int RPI = 1024 / KCB;             // rows per load instruction
   static constexpr int MAXSEG = ((WROWS + TT * 16) / RPI + NW - 1) / NW;
-  static_assert(STEPS % NW == 0 && SPW >= 1, "a chunk must give every wavefront k-steps");
+  static_assert(NW % NP == 0 && STEPS % NP == 0 && RT % RH == 0, "wavefront split");
   static_assert(PIECES >= 16 && KCB <= 1024, "swizzle needs at least 16 pieces per row");
   static_assert(NSLOT >= 2, "ring");
+  static_assert(NP * kQuads * 16 <= kLdsBytes, "the partials fit the ring");
 
   lds_char* ring;           // kLdsBytes of LDS
   const char* gp[MAXSEG];   // this lane's source for chunk 0 of each of its segments
   uint32_t dst[MAXSEG];     // segment offset inside a slot (wave-uniform)
   uint32_t kb[MAXSEG];      // byte offset of this lane's piece inside a chunk
   bool rv[MAXSEG];          // this lane's row exists
-  int nseg, nwseg, nC, K, wave, r16, kq;
-  f32x4 acc[RT][TT];
+  int nseg, nwseg, nC, K, wave, kp, rh, r16, kq;
+  f32x4 acc[RTW][TT];
 
   __device__ __forceinline__ void issue(int c) {
     const uint32_t cb = (uint32_t)c * KCB;
@@ -238,12 +247,15 @@ struct GemmLds {
     }
   }
 
-  // Sets up this wavefront's segments and issues the first NSLOT - 1 chunks.
+  // Sets up this wavefront's segments for the k range [k_begin, k_begin + K_)
+  // of rows [row0, row0 + rows) and issues the first NSLOT - 1 chunks.
   __device__ __forceinline__ void start(const uint16_t* __restrict__ x, int64_t ldx,
                                         const uint16_t* __restrict__ W, int64_t ldw, int M,
-                                        int K_, int row0, int rows, char* lds) {
+                                        int k_begin, int K_, int row0, int rows, char* lds) {
     const int lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    kp = wave % NP;
+    rh = wave / NP;
     r16 = lane & 15;
     kq = lane >> 4;
     K = K_;
@@ -263,13 +275,13 @@ struct GemmLds {
       const int p = q ^ (lrow & 15);
       rv[i] = isw ? r < rows : r < M;
       const int rr = rv[i] ? r : 0;
-      gp[i] = isw ? reinterpret_cast<const char*>(W + (size_t)(row0 + rr) * ldw) + 16 * p
-                  : reinterpret_cast<const char*>(x + (size_t)rr * ldx) + 16 * p;
+      gp[i] = isw ? reinterpret_cast<const char*>(W + (size_t)(row0 + rr) * ldw + k_begin) + 16 * p
+                  : reinterpret_cast<const char*>(x + (size_t)rr * ldx + k_begin) + 16 * p;
       kb[i] = 16 * p;
       dst[i] = __builtin_amdgcn_readfirstlane(((isw ? 0 : WROWS) + (sidx < wseg ? sidx : sidx - wseg) * RPI) * KCB);
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int c = 0; c < NSLOT - 1 && c < nC; ++c) issue(c);
@@ -280,25 +292,25 @@ struct GemmLds {
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
-      const int ks = wave * SPW + j;
+      const int ks = kp * SPW + j;
       const int k0 = c * KE + ks * 32;
       if (k0 < K) {
         const int off = 16 * ((ks * 4 + kq) ^ r16);
-        u32x4 a[RT], b[TT];
+        u32x4 a[RTW], b[TT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          a[rt] = *reinterpret_cast<const lds_u32x4*>(slot + (rt * 16 + r16) * KCB + off);
+        for (int rt = 0; rt < RTW; ++rt)
+          a[rt] = *reinterpret_cast<const lds_u32x4*>(slot + ((rh * RTW + rt) * 16 + r16) * KCB + off);
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
           b[tt] = *reinterpret_cast<const lds_u32x4*>(slot + (WROWS + tt * 16 + r16) * KCB + off);
         if (k0 + 32 > K && k0 + 8 * kq >= K) {
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) a[rt] = zero;
+          for (int rt = 0; rt < RTW; ++rt) a[rt] = zero;
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt) b[tt] = zero;
         }
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = mfma_bf16(a[rt], b[tt], acc[rt][tt]);
       }
@@ -319,21 +331,25 @@ struct GemmLds {
     wg_barrier();
   }
 
+  // This wavefront's partial tiles: red[(kp * kQuads) + quad].
   __device__ __forceinline__ void stash(f32x4* red) const {
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) red[((wave * RT + rt) * TT + tt) * 64 + lane] = acc[rt][tt];
+      for (int tt = 0; tt < TT; ++tt)
+        red[((kp * RT + rh * RTW + rt) * TT + tt) * 64 + lane] = acc[rt][tt];
   }
 
+  // Sum over the k-partials, in k-slice order, of quad q < kQuads.
   __device__ static __forceinline__ f32x4 gather(const f32x4* red, int q) {
     f32x4 s = red[q];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) s += red[w * kQuads + q];
+    for (int w = 1; w < NP; ++w) s += red[w * kQuads + q];
     return s;
   }
 
+  // Token and first row (relative to row0) of quad q.
   __device__ static __forceinline__ void quad_coords(int q, int& m, int& r) {
     const int rt = q / (TT * 64), tt = (q / 64) % TT, ln = q & 63;
     m = tt * 16 + (ln & 15);
@@ -348,6 +364,13 @@ struct GemmLds {
 template <int RT, int TT>
 using GemmLdsFor = GemmLds<RT, TT, (TT == 1 && RT == 1 ? 1024 : 512),
                            (TT == 1 ? (RT == 1 ? 3 : 4) : TT == 2 ? 4 : 3)>;
+
+// Split-K tiles for more than 32 tokens: 64 rows (four row tiles) per
+// workgroup over half of K, 256-byte row segments in four slots; wavefronts
+// split into four k-steps by two row groups.
+constexpr int kSplitRows = 64;
+template <int TT>
+using GemmLdsSplit = GemmLds<4, TT, 256, 4>;
 
 // Rows of W per workgroup for N output rows: spread N over 256 workgroups (one
 // per compute unit), a multiple of 4, at most 32 (two 16-row MFMA tiles).

@@ -16,11 +16,23 @@ struct GemmParams {
 };
 
 // Workspace of the fused kernel: a small header, then the new-prefix mailbox
-// [M][H/2] 32-bit words (a bf16 pair each). Every mailbox word holds the
-// sentinel between calls; a call's GEMM workgroups overwrite it with the new
-// prefix and the owning workgroup re-arms it after reading.
-constexpr unsigned kMailboxSentinel = 0x80000000u;  // bf16 pair (+0.0, -0.0)
+// [M][H/2] 32-bit words (a bf16 pair each), then (beyond 32 tokens) the
+// split-K hand-off: per 64-row group, the first K half's FP32 partial
+// products, one 16-byte quad per MFMA output quad. Every word after the header
+// holds the sentinel between calls; a producer overwrites it and the consumer
+// re-arms it after reading. 0x80000000 is the bf16 pair (+0.0, -0.0), which a
+// new-prefix pair never holds, and the FP32 -0.0, which a stored partial
+// never holds (producers store +0.0 for a zero).
+constexpr unsigned kMailboxSentinel = 0x80000000u;
 constexpr size_t kWorkspaceHeader = 256;
+
+// Split-K hand-off bytes for M tokens and H rows (0 when no split is used).
+inline size_t split_partial_bytes(int M, int H) {
+  if (M <= 32) return 0;
+  const size_t groups = (size_t)(H + 63) / 64;
+  const size_t quads = 4 * (size_t)((M + 15) / 16) * 64;  // four row tiles x token tiles
+  return groups * quads * 16;
+}
 
 struct FusedWorkspace {
   unsigned error;  // nonzero after an owner gave up waiting (results invalid)
@@ -34,7 +46,10 @@ struct FusedParams {
   int64_t ldw;
   int K;
   FusedWorkspace* ws;
-  unsigned* mailbox;  // [M][H / 2]
+  unsigned* mailbox;   // [M][H / 2]
+  unsigned* partials;  // split-K hand-off (see above)
+  int ng;              // split-K row groups (0: no split)
+  int k_half;          // split point of K
 };
 
 hipError_t launch_wsgemm(const GemmParams& p, hipStream_t stream);

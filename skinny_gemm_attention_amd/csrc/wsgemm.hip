@@ -9,13 +9,12 @@ template <int RT, int TT>
 __global__ __launch_bounds__(512) void wsgemm_kernel(GemmParams p, int R) {
   using C = GemmLdsFor<RT, TT>;
   static_assert(C::NT == 512, "launch bounds");
-  static_assert(C::NW * C::kQuads * sizeof(f32x4) <= C::kLdsBytes, "partials fit the ring");
   __shared__ __attribute__((aligned(16))) char lds[C::kLdsBytes];
   f32x4* red = reinterpret_cast<f32x4*>(lds);  // reused once the ring is drained
   const int row0 = blockIdx.x * R;
   const int rows = min(R, p.N - row0);
   C core;
-  core.start(p.x, p.ldx, p.W, p.ldw, p.M, p.K, row0, rows, lds);
+  core.start(p.x, p.ldx, p.W, p.ldw, p.M, 0, p.K, row0, rows, lds);
   core.finish();
   core.stash(red);
   lds_barrier();

@@ -60,7 +60,11 @@ def test_strerror_and_workspace(lib):
     for c, word in codes.items():
         assert word in lib.attnres_strerror(c)
     assert b"unknown" in lib.attnres_strerror(-99)
-    assert lib.attnres_oproj_workspace_size(64, 7168, 8) == 256 + 64 * 7168 * 2
+    # header, bf16 mailbox rows and, beyond 32 tokens, the split-K hand-off
+    # (per 64-row group one 16-byte quad per MFMA output quad)
+    assert lib.attnres_oproj_workspace_size(32, 7168, 8) == 256 + 32 * 7168 * 2
+    assert lib.attnres_oproj_workspace_size(64, 7168, 8) == 256 + 64 * 7168 * 2 + 112 * 1024 * 16
+    assert lib.attnres_oproj_workspace_size(33, 8192, 8) == 256 + 33 * 8192 * 2 + 128 * 768 * 16
     assert lib.attnres_oproj_workspace_size(1, 8, 0) == 512
     # host-side rejections of the init call (no launch happens)
     assert lib.attnres_oproj_workspace_init(None, 1024, None) == -5

@@ -2,10 +2,12 @@
 with the FP64 oracle, on the three decode-step workloads and edge cases.
 
 The o-projection output is the AttnRes delta (vLLM oproj.prepared page),
-rounded to bf16 with -0.0 made +0.0 (gemm.ws_gemm page, positive_zero), so the
-fused call must equal wsgemm_run followed by attnres_run bit for bit. Against
-the oracle the FP32 accumulation of the GEMM may move a delta by one bf16 ulp,
-so out and the new prefix are held to the two-ulp / 5e-3 relative-L2 bound.
+rounded to bf16 with -0.0 made +0.0 (gemm.ws_gemm page, positive_zero), so up
+to 32 tokens the fused call must equal wsgemm_run followed by attnres_run bit
+for bit. Beyond 32 tokens the fused call splits K over two workgroups, which
+sums the projection in another order, so there the two agree up to rounding.
+Against the oracle the FP32 accumulation of the GEMM may move a delta by one
+bf16 ulp, so out and the new prefix are held to the derived bounds.
 """
 from __future__ import annotations
 
@@ -103,8 +105,13 @@ def test_fused_equals_gemm_then_attnres(configs, cfg):
     s = configs[cfg]
     for final in (0, 1):
         a, b = fused(s, final=final), split(s, final=final)
-        for k in ("out", "prefix", "blocks", "aux"):
-            assert np.array_equal(a[k], b[k]), f"cfg{cfg} final={final}: {k} differs"
+        if s.M <= 32:
+            for k in ("out", "prefix", "blocks", "aux"):
+                assert np.array_equal(a[k], b[k]), f"cfg{cfg} final={final}: {k} differs"
+        else:  # split K: the same values up to the FP32 summation order
+            assert_new_prefix_close(a["prefix"], b["prefix"], s.prefix, s.has_delta,
+                                    f"cfg{cfg} final={final} fused vs split prefix")
+            assert np.array_equal(a["aux"], a["prefix"]) and np.array_equal(b["aux"], b["prefix"])
 
 
 @pytest.mark.parametrize("M,K,H,nb,cap,write,has_delta", [
@@ -114,6 +121,9 @@ def test_fused_equals_gemm_then_attnres(configs, cfg):
     (17, 4096, 7168, 8, 8, 0, 0),   # overwrite a scored slot, no old prefix
     (1, 0, 7168, 1, 1, -1, 1),      # K = 0: delta = +0.0
     (64, 7168, 8192, 8, 9, 8, 1),   # widest rows
+    (33, 1000, 1024, 3, 4, 3, 1),   # split K: ragged second half, 33 tokens
+    (48, 264, 7168, 2, 3, -1, 1),   # split K: a second half of one k-step
+    (40, 2056, 520, 1, 2, 1, 0),    # split K: ragged last row group
 ])
 def test_fused_edges(M, K, H, nb, cap, write, has_delta):
     s = synth.decode_step(M, K, nb, H=H, cap=cap, write=write, has_delta=has_delta, seed=M + K)
