@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
     }
     {
       C core;
-      core.start(f.x, f.ldx, f.W, f.ldw, M, kbeg, klen, row0, rows, sm.ring);
+      core.start(f.x, f.ldx, f.W, f.ldw, M, kbeg, klen, row0, rows, sm.ring, SPLIT ? rg : 0);
       core.finish();
       core.stash(red);
     }

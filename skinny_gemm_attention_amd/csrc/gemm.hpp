@@ -228,11 +228,17 @@ struct GemmLds {
   uint32_t dst[MAXSEG];     // segment offset inside a slot (wave-uniform)
   uint32_t kb[MAXSEG];      // byte offset of this lane's piece inside a chunk
   bool rv[MAXSEG];          // this lane's row exists
-  int nseg, nwseg, nC, K, wave, kp, rh, r16, kq;
+  int nseg, nwseg, nC, rot, K, wave, kp, rh, r16, kq;
   f32x4 acc[RTW][TT];
 
+  // Chunks are consumed in the order rot, rot + 1, ..., wrapping around.
+  __device__ __forceinline__ int phys(int c) const {
+    const int p = c + rot;
+    return p >= nC ? p - nC : p;
+  }
+
   __device__ __forceinline__ void issue(int c) {
-    const uint32_t cb = (uint32_t)c * KCB;
+    const uint32_t cb = (uint32_t)phys(c) * KCB;
     lds_char* slot = ring + (c % NSLOT) * SLOT;
 #pragma unroll
     for (int i = 0; i < MAXSEG; ++i) {
@@ -248,10 +254,13 @@ struct GemmLds {
   }
 
   // Sets up this wavefront's segments for the k range [k_begin, k_begin + K_)
-  // of rows [row0, row0 + rows) and issues the first NSLOT - 1 chunks.
+  // of rows [row0, row0 + rows) and issues the first NSLOT - 1 chunks. With
+  // rot_ > 0 the chunks are taken in rotated order (workgroups that share x
+  // then read different parts of it at a time); the order is fixed per call.
   __device__ __forceinline__ void start(const uint16_t* __restrict__ x, int64_t ldx,
                                         const uint16_t* __restrict__ W, int64_t ldw, int M,
-                                        int k_begin, int K_, int row0, int rows, char* lds) {
+                                        int k_begin, int K_, int row0, int rows, char* lds,
+                                        int rot_ = 0) {
     const int lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     kp = wave % NP;
@@ -261,6 +270,7 @@ struct GemmLds {
     K = K_;
     ring = (lds_char*)lds;
     nC = (K + KE - 1) / KE;
+    rot = nC > 0 ? rot_ % nC : 0;
     const int wseg = (rows + RPI - 1) / RPI, xseg = (M + RPI - 1) / RPI;
     const int S = wseg + xseg;
     nseg = wave < S ? (S - wave + NW - 1) / NW : 0;
@@ -293,7 +303,7 @@ struct GemmLds {
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int ks = kp * SPW + j;
-      const int k0 = c * KE + ks * 32;
+      const int k0 = phys(c) * KE + ks * 32;
       if (k0 < K) {
         const int off = 16 * ((ks * 4 + kq) ^ r16);
         u32x4 a[RTW], b[TT];
