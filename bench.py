@@ -19,7 +19,10 @@ Protocol:
     the host cores, in the same process.
 
 Prints one JSON line. `--config` picks another fused workload (0: M=1 K=1024
-nb=1; 2: M=64 K=8192 nb=8 with a block write) for side measurements.
+nb=1; 2: M=64 K=8192 nb=8 with a block write) for side measurements; `--config
+3` (attnres_run, T=256, nb = 0..8, final boundary) and `--config 4`
+(wsgemm_run, K=7168, N=4096, M = 1, 8, 16, 64) print one JSON line per case,
+timed the same way.
 """
 from __future__ import annotations
 
@@ -73,12 +76,108 @@ def kernel_digest() -> str:
     return h.hexdigest()
 
 
+def graph_time_us(torch, step, steps, warmup):
+    """Average µs per call of `steps` calls captured in one HIP graph (replayed
+    once untimed, once timed between HIP events on the launch stream)."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(steps):
+                step(i)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def side_configs(args, np, torch, sga, synth):
+    """Standalone AttnRes (T=256, nb = 0..8, final boundary) or standalone
+    GEMM (K=7168, N=4096, M = 1, 8, 16, 64): one JSON line per case."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    steps = min(args.steps, 400)
+    if args.config == 3:
+        T = 256
+        for nb in range(9):
+            s = synth.config_inputs(3, nb=nb)
+            row = 2 * H
+            nbytes = 3 * row + T * row * (1 + 1 + nb + 1 + 1 + 1)  # delta, prefix, blocks, writes
+            L = max(2, math.ceil(FOOTPRINT / (T * row * (nb + 5))))
+            base = dict(delta=up(s.delta), prefix=up(s.prefix), blocks=up(s.blocks))
+            nq = [up(s.norm), up(s.query), up(s.out_norm)]
+            cp = []
+            for i in range(L):
+                t = {k: v.clone() for k, v in base.items()}
+                t["out"] = torch.zeros((T, H), dtype=torch.int16, device=dev)
+                t["aux"] = torch.zeros((T, H), dtype=torch.int16, device=dev)
+                cp.append(t)
+            torch.cuda.synchronize()
+
+            def step(i):
+                t = cp[i % L]
+                sga.attnres_run(t["delta"], t["prefix"], t["blocks"], *nq, t["out"], t["aux"],
+                                nb=nb, write=-1, has_delta=1, final_boundary=1)
+
+            us = graph_time_us(torch, step, steps, args.warmup)
+            print(json.dumps({"metric": "attnres_run µs/call + achieved HBM GB/s",
+                              "value": round(nbytes / us / 1e3, 1), "unit": "GB/s",
+                              "us_per_call": round(us, 3), "pct_of_hbm_peak":
+                              round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1),
+                              "algorithmic_bytes": nbytes, "dtype": "bf16",
+                              "data": "synthetic", "config": {
+                                  "workload": f"attnres_run T={T} H={H} nb={nb} final=1 aux=1",
+                                  "layer_copies": L}}), flush=True)
+            del cp
+    else:
+        N, K = 4096, 7168
+        for M in (1, 8, 16, 64):
+            x, W = synth.gemm_inputs(M, N, K)
+            nbytes = 2 * N * K + 2 * M * K + 2 * M * N
+            L = max(2, math.ceil(FOOTPRINT / (2 * N * K)))
+            xg = up(x)
+            Ws = [up(W)]
+            for i in range(1, L):
+                Ws.append(Ws[0].clone())
+            ys = [torch.zeros((M, N), dtype=torch.int16, device=dev) for _ in range(L)]
+            torch.cuda.synchronize()
+
+            def step(i):
+                sga.wsgemm_run(xg, Ws[i % L], ys[i % L])
+
+            us = graph_time_us(torch, step, steps, args.warmup)
+            print(json.dumps({"metric": "wsgemm_run µs/call + achieved HBM GB/s",
+                              "value": round(nbytes / us / 1e3, 1), "unit": "GB/s",
+                              "us_per_call": round(us, 3), "pct_of_hbm_peak":
+                              round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1),
+                              "algorithmic_bytes": nbytes, "dtype": "bf16",
+                              "data": "synthetic", "config": {
+                                  "workload": f"wsgemm_run M={M} N={N} K={K}",
+                                  "layer_copies": L}}), flush=True)
+            del Ws, ys
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1, choices=sorted(WORKLOADS))
+    ap.add_argument("--config", type=int, default=1, choices=sorted(WORKLOADS) + [3, 4])
     ap.add_argument("--final", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bounded host time for the oracle baseline (0 skips it)")
@@ -96,6 +195,10 @@ def main():
 
     import skinny_gemm_attention_amd as sga
     import synth
+
+    if args.config in (3, 4):
+        side_configs(args, np, torch, sga, synth)
+        return
 
     cfg = WORKLOADS[args.config]
     M, K, nb, cap, write, has_delta = (cfg[k] for k in ("M", "K", "nb", "cap", "write",
