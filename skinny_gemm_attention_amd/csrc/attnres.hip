@@ -12,7 +12,8 @@ namespace attnres {
 template <int NT>
 __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
   constexpr int NW = TokenShape<NT>::NW, NCH = TokenShape<NT>::NCH;
-  __shared__ float lds_pre[NW * 16], lds_post[NW * 4], lds_fin[NW];
+  __shared__ float lds_pre[wg_sum_lds<16, NW>], lds_post[wg_sum_lds<4, NW>],
+      lds_fin[wg_sum_lds<1, NW>];
   const int t = blockIdx.x, tid = threadIdx.x, CH = a.H >> 3;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 

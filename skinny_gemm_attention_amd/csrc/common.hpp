@@ -162,28 +162,114 @@ __device__ __forceinline__ float wave_sum63(float v) {
 // The same sum, returned to every lane.
 __device__ __forceinline__ float wave_sum(float v) { return readlane(wave_sum63(v), 63); }
 
+// The value of lane (l ^ X) (wave64), all VALU: X = 1, 2 are DPP quad
+// permutations; X = 4, 8 take row_shl / row_shr by X (whichever points at the
+// partner); X = 16, 32 use gfx950's v_permlane16_swap / v_permlane32_swap,
+// which exchange rows 0 <-> 1 and 2 <-> 3 / lane halves.
+template <int X>
+__device__ __forceinline__ float xor_lane(float v) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (X == 1) {
+    return dpp<0xB1>(v);
+  } else if constexpr (X == 2) {
+    return dpp<0x4E>(v);
+  } else if constexpr (X == 4 || X == 8) {
+    const float up = dpp<0x100 + X>(v);    // row_shl: lane i reads lane i + X
+    const float down = dpp<0x110 + X>(v);  // row_shr: lane i reads lane i - X
+    return (lane & X) ? down : up;
+  } else if constexpr (X == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else {
+    static_assert(X == 32, "xor partner");
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  }
+}
+
+// Sums K = 2^n values over the 64 lanes of a wavefront with about 2K lane
+// exchanges instead of 6K: at level L < n each lane keeps half of its values
+// (the half selected by lane bit L) and adds its partner's (lane ^ 2^L) copy
+// of that half; the levels n..5 add the single remaining value across the
+// partner. Every addition pairs a lane with a partner that computes the same
+// sum with the operands swapped, so all lanes holding a value agree bit for
+// bit. On return v[0] of lane l holds the total of value index
+// k(l) = sum_L bit_L(l) * (K >> (L + 1)), i.e. the bit reverse of l mod K.
+template <int K, int L = 0>
+__device__ __forceinline__ void wave_multi_sum(float (&v)[K]) {
+  if constexpr (L < 6) {
+    const int lane = threadIdx.x & 63;
+    constexpr int n = K >> L;  // values still held per lane (power of two, >= 1)
+    if constexpr (n > 1) {
+      const bool hi = (lane >> L) & 1;
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) {
+        const float keep = hi ? v[n / 2 + i] : v[i];
+        const float send = hi ? v[i] : v[n / 2 + i];
+        v[i] = keep + xor_lane<(1 << L)>(send);
+      }
+    } else {
+      v[0] += xor_lane<(1 << L)>(v[0]);
+    }
+    wave_multi_sum<K, L + 1>(v);
+  }
+}
+
+// LDS floats wg_sum<K, NW> needs: the wavefront totals, then the K totals.
+template <int K, int NW>
+constexpr int wg_sum_lds = NW * K + K;
+
 // Sums K per-thread partials over a workgroup of NW wavefronts: wavefront sums
-// (wave_sum63), then the NW wavefront totals in wavefront order. Every thread
-// gets the totals in v. `lds` holds NW*K floats and must not be reused by
-// another reduction of the same workgroup until all threads have returned.
-// Contains a workgroup barrier: call from uniform control flow.
+// (wave_sum63 for K <= 4, wave_multi_sum beyond), then the NW wavefront
+// totals in wavefront order (for K >= 4 formed once by K threads and read
+// back by every thread). Every thread gets the totals in v. `lds` holds wg_sum_lds<K, NW>
+// floats and must not be reused by another reduction of the same workgroup
+// until all threads have returned. Contains workgroup barriers: call from
+// uniform control flow.
 template <int K, int NW>
 __device__ __forceinline__ void wg_sum(float (&v)[K], float* lds) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float t[K];
+  if constexpr (K <= 4) {
+    float t[K];
 #pragma unroll
-  for (int k = 0; k < K; ++k) t[k] = wave_sum63(v[k]);
-  if (lane == 63) {
+    for (int k = 0; k < K; ++k) t[k] = wave_sum63(v[k]);
+    if (lane == 63) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) lds[wave * K + k] = t[k];
+      for (int k = 0; k < K; ++k) lds[wave * K + k] = t[k];
+    }
+  } else {
+    static_assert((K & (K - 1)) == 0 && K <= 64, "a power of two");
+    float t[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) t[k] = v[k];
+    wave_multi_sum<K>(t);
+    if (lane < K) {
+      int k = 0;  // bit reverse of lane within log2(K) bits
+#pragma unroll
+      for (int b = 0; (1 << b) < K; ++b) k |= ((lane >> b) & 1) * (K >> (b + 1));
+      lds[wave * K + k] = t[0];
+    }
   }
   lds_barrier();
+  if constexpr (K < 4) {  // few values: every thread adds the wavefront totals
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    float s = lds[k];
+    for (int k = 0; k < K; ++k) {
+      float s = lds[k];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) s += lds[w * K + k];
-    v[k] = s;
+      for (int w = 1; w < NW; ++w) s += lds[w * K + k];
+      v[k] = s;
+    }
+  } else {  // K threads add them once, every thread reads the K totals
+    if ((int)threadIdx.x < K) {
+      const int k = threadIdx.x;
+      float s = lds[k];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) s += lds[w * K + k];
+      lds[NW * K + k] = s;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = lds[NW * K + k];
   }
 }
 

@@ -90,7 +90,8 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
   };
   __shared__ __attribute__((aligned(16))) Smem sm;
   f32x4* red = reinterpret_cast<f32x4*>(sm.ring);
-  __shared__ float lds_pre[NW * (4 * KT > 16 ? 4 * KT : 16)], lds_fin[NW];
+  __shared__ float lds_pre[wg_sum_lds<(4 * KT > 16 ? 4 * KT : 16), NW>],
+      lds_fin[wg_sum_lds<1, NW>];
 
   const AttnParams& a = f.a;
   const int g = blockIdx.x, tid = threadIdx.x, CH = a.H >> 3;
