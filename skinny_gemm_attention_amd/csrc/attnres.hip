@@ -62,10 +62,10 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
       float pf[8], df[8];
       unpack8(p[j], pf);
       unpack8(d[j], df);
-      nbits[j].x = pack2(add_round_odd(pf[0], df[0]), add_round_odd(pf[1], df[1]));
-      nbits[j].y = pack2(add_round_odd(pf[2], df[2]), add_round_odd(pf[3], df[3]));
-      nbits[j].z = pack2(add_round_odd(pf[4], df[4]), add_round_odd(pf[5], df[5]));
-      nbits[j].w = pack2(add_round_odd(pf[6], df[6]), add_round_odd(pf[7], df[7]));
+      nbits[j].x = pack2(add_bf16_exact(pf[0], df[0]), add_bf16_exact(pf[1], df[1]));
+      nbits[j].y = pack2(add_bf16_exact(pf[2], df[2]), add_bf16_exact(pf[3], df[3]));
+      nbits[j].z = pack2(add_bf16_exact(pf[4], df[4]), add_bf16_exact(pf[5], df[5]));
+      nbits[j].w = pack2(add_bf16_exact(pf[6], df[6]), add_bf16_exact(pf[7], df[7]));
     } else {
       nbits[j] = d[j];
     }

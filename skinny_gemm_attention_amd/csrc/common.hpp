@@ -56,22 +56,13 @@ __device__ __forceinline__ unsigned positive_zero(unsigned w) {
   return w;
 }
 
-// a + b rounded to odd at float precision. With a and b bfloat16 values the
-// result, rounded once more to bfloat16 (nearest even), is the correctly
-// rounded bfloat16 sum: round-to-odd with 24 bits keeps enough information for
-// the 8-bit rounding that follows (a standard double-rounding-safe scheme).
-// TwoSum (Knuth) gives the exact error of the float sum.
-__device__ __forceinline__ float add_round_odd(float a, float b) {
-  const float s = a + b;
-  const float bb = s - a;
-  const float err = (a - (s - bb)) + (b - bb);
-  unsigned u = __float_as_uint(s);
-  if (err != 0.0f && (u & 1u) == 0u) {
-    const bool away = (err > 0.0f) == (s > 0.0f);  // true value lies farther from zero
-    u = away ? u + 1u : u - 1u;
-  }
-  return __uint_as_float(u);
-}
+// a + b for bfloat16 a and b, as a float whose rounding to bfloat16 (nearest
+// even) is the correctly rounded bfloat16 sum. One float addition suffices:
+// float carries 24 significant bits, at least 2 * 8 + 2, and for addition of
+// two 8-bit-precision values rounding first to 24 bits and then to 8 never
+// differs from rounding once (the double-rounding bound for addition,
+// Figueroa 1995).
+__device__ __forceinline__ float add_bf16_exact(float a, float b) { return a + b; }
 
 // Reciprocal RMS of a row from its sum of squares (attn_res.kernel page,
 // helper rstd): rsqrt(sum_sq / H + eps), v_rsq_f32.

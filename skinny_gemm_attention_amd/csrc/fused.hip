@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
           unpack8(oprefix, pf);
           unpack8(y, yf);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) r[e] = add_round_odd(pf[e], yf[e]);
+          for (int e = 0; e < 8; ++e) r[e] = add_bf16_exact(pf[e], yf[e]);
           nv = pack8(r);
         }
         const size_t col = (size_t)row0 + 8 * oj;
@@ -241,10 +241,10 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
         const unsigned y01 = positive_zero(pack2(s[i].x, s[i].y)), y23 = positive_zero(pack2(s[i].z, s[i].w));
         u32x2 nv;
         if (a.has_delta) {
-          nv.x = pack2(add_round_odd(bf_lo(qprefix[i].x), bf_lo(y01)),
-                       add_round_odd(bf_hi(qprefix[i].x), bf_hi(y01)));
-          nv.y = pack2(add_round_odd(bf_lo(qprefix[i].y), bf_lo(y23)),
-                       add_round_odd(bf_hi(qprefix[i].y), bf_hi(y23)));
+          nv.x = pack2(add_bf16_exact(bf_lo(qprefix[i].x), bf_lo(y01)),
+                       add_bf16_exact(bf_hi(qprefix[i].x), bf_hi(y01)));
+          nv.y = pack2(add_bf16_exact(bf_lo(qprefix[i].y), bf_lo(y23)),
+                       add_bf16_exact(bf_hi(qprefix[i].y), bf_hi(y23)));
         } else {
           nv = u32x2{y01, y23};
         }
