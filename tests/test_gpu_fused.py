@@ -146,3 +146,75 @@ def test_fused_deterministic(configs):
     a, b = fused(s, final=0), fused(s, final=0)
     for k in ("out", "prefix", "blocks"):
         assert np.array_equal(a[k], b[k]), k
+
+
+def _fused_buffers(s, *, aux=True):
+    sga = lib()
+    b = dict(x=up(s.x), W=up(s.W), norm=up(s.norm), query=up(s.query), out_norm=up(s.out_norm),
+             prefix=up(s.prefix), blocks=up(s.blocks),
+             out=torch.full((s.M, s.H), POISON, dtype=torch.int16, device=DEV),
+             aux=torch.full((s.M, s.H), POISON, dtype=torch.int16, device=DEV) if aux else None,
+             ws=sga.make_workspace(s.M, s.H, s.nb, DEV))
+    return b
+
+
+def _fused_call(s, b, *, final, stream=None):
+    lib().attnres_oproj_run(b["x"], b["W"], b["prefix"], b["blocks"], b["norm"], b["query"],
+                            b["out_norm"], b["out"], b["aux"], b["ws"], nb=s.nb, write=s.write,
+                            has_delta=s.has_delta, final_boundary=final, eps=s.eps,
+                            out_eps=s.out_eps, stream=stream)
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_fused_in_a_hip_graph(configs, cfg):
+    """One call captured in a HIP graph and replayed three times, with eager
+    restores of the in/out state between replays: every replay equals the
+    eager call bit for bit and leaves the workspace re-armed."""
+    s = configs[cfg]
+    eager = fused(s, final=0)
+    b = _fused_buffers(s)
+    prefix0, blocks0 = b["prefix"].clone(), b["blocks"].clone()
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            _fused_call(s, b, final=0)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        b["prefix"].copy_(prefix0)
+        b["blocks"].copy_(blocks0)
+        b["out"].fill_(POISON)
+        b["aux"].fill_(POISON)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        for k in ("out", "prefix", "blocks", "aux"):
+            assert np.array_equal(down(b[k]), eager[k]), f"cfg{cfg} replay {rep}: {k}"
+        words = b["ws"].cpu().numpy().view(np.uint32)
+        assert np.all(words[:64] == 0) and np.all(words[64:] == 0x80000000), f"replay {rep}"
+
+
+def test_fused_on_two_streams_at_once():
+    """Two calls with their own workspaces on two streams, not synchronised
+    with each other: each equals its own single-stream result."""
+    sa = synth.decode_step(8, 4096, 4, seed=21)
+    sb = synth.decode_step(64, 4096, 8, cap=9, write=8, seed=22)
+    ea, eb = fused(sa, final=0), fused(sb, final=1)
+    ba, bb = _fused_buffers(sa), _fused_buffers(sb)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(2):  # the second round reuses the re-armed workspaces
+        ba["prefix"].copy_(up(sa.prefix))
+        bb["prefix"].copy_(up(sb.prefix))
+        bb["blocks"].copy_(up(sb.blocks))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            _fused_call(sa, ba, final=0)
+        with torch.cuda.stream(s2):
+            _fused_call(sb, bb, final=1)
+        torch.cuda.synchronize()
+        for k in ("out", "prefix", "blocks", "aux"):
+            assert np.array_equal(down(ba[k]), ea[k]), f"stream 1: {k}"
+            assert np.array_equal(down(bb[k]), eb[k]), f"stream 2: {k}"
