@@ -107,6 +107,35 @@ __device__ __forceinline__ void wait_vmem() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// vmcnt(N) lgkmcnt(0): this wavefront's memory operations except the N most
+// recent have completed, and its LDS operations too.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);  // vmcnt(N) lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// vmcnt(n) lgkmcnt(0) for a wave-uniform 0 <= n <= N (waitcnt immediates
+// exist only at compile time, hence the chain).
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+  if constexpr (N == 0) {
+    wait_vmem_n<0>();
+  } else {
+    if (n >= N) wait_vmem_n<N>();
+    else wait_vmem_upto<N - 1>(n);
+  }
+}
+
+// Workgroup barrier without a memory fence (the waits above are explicit).
+__device__ __forceinline__ void wg_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Workgroup barrier for LDS traffic: waits for this wavefront's LDS operations
 // (lgkmcnt(0)) but not for its global stores, which __syncthreads() would
 // also drain (vmcnt(0)). Call from uniform control flow.

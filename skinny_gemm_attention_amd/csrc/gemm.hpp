@@ -50,33 +50,6 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 //   * One workgroup barrier per chunk: after it, chunk c is complete (each
 //     wavefront waited for its own loads of c) and every wavefront has
 //     finished reading chunk c - 1, whose slot is refilled next.
-template <int N>
-__device__ __forceinline__ void wait_vmem_n() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);  // vmcnt(N) lgkmcnt(0)
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// vmcnt(n) lgkmcnt(0) for a wave-uniform 0 <= n <= N (waitcnt immediates
-// exist only at compile time, hence the chain).
-template <int N>
-__device__ __forceinline__ void wait_vmem_upto(int n) {
-  if constexpr (N == 0) {
-    wait_vmem_n<0>();
-  } else {
-    if (n >= N) wait_vmem_n<N>();
-    else wait_vmem_upto<N - 1>(n);
-  }
-}
-
-// Workgroup barrier without a memory fence (the waits above are explicit).
-__device__ __forceinline__ void wg_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // Cache-policy operand of global_load_lds: the non-temporal bit.
 constexpr int kCacheNT = 2;
 

@@ -130,3 +130,29 @@ def test_attnres_empty():
     bl = torch.zeros((0, 1, s.H), dtype=torch.int16, device=DEV)
     sga.attnres_run(z, z, bl, up(s.norm), up(s.query), up(s.out_norm), z, None, nb=1)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T,H,nb,cap,write,has_delta,final,aux,pad,slot_major", [
+    (257, 7168, 4, 5, 2, 0, 0, True, 0, False),    # odd T, overwrite a scored slot, no old prefix
+    (300, 1000, 3, 4, 3, 1, 1, False, 8, False),   # rows not a multiple of 512 columns, padded rows
+    (258, 4104, 8, 9, 8, 1, 0, True, 0, True),     # slot-major blocks, block write after the scored slots
+    (260, 8192, 8, 8, 0, 1, 1, True, 0, False),    # widest rows, all slots scored
+    (512, 2048, 0, 1, 0, 0, 1, True, 0, False),    # nb = 0, delta path off
+])
+def test_attnres_many_tokens(T, H, nb, cap, write, has_delta, final, aux, pad,
+                                          slot_major):
+    """Many tokens (more than half the compute units), odd counts, widths that
+    are not a multiple of 512 columns, padded and slot-major layouts."""
+    s = synth.decode_step(T, None, nb, H=H, cap=cap, seed=T + H + nb)
+    r = run(s, nb=nb, write=write, has_delta=has_delta, final=final, aux=aux, pad=pad,
+            slot_major=slot_major)
+    if slot_major:
+        ref = oracle.attnres(s.delta, s.prefix, s.blocks, s.norm, s.query, s.out_norm, nb=nb,
+                             write=write, has_delta=has_delta, final=final, eps=s.eps,
+                             out_eps=s.out_eps, aux=aux, nthreads=16)
+        assert_bf16_close(r["out"], ref.out, "slot-major out")
+        assert np.array_equal(r["prefix"], ref.prefix)
+        assert np.array_equal(r["blocks"], ref.blocks)
+    else:
+        check(s, r, nb=nb, write=write, has_delta=has_delta, final=final, aux=aux,
+              what=f"T={T} H={H} nb={nb}")
