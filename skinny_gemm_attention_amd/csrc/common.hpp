@@ -241,7 +241,7 @@ constexpr int wg_sum_lds = NW * K + K;
 
 // Sums K per-thread partials over a workgroup of NW wavefronts: wavefront sums
 // (wave_sum63 for K <= 4, wave_multi_sum beyond), then the NW wavefront
-// totals in wavefront order (for K >= 4 formed once by K threads and read
+// totals in wavefront order (for K > 4 formed once by K threads and read
 // back by every thread). Every thread gets the totals in v. `lds` holds wg_sum_lds<K, NW>
 // floats and must not be reused by another reduction of the same workgroup
 // until all threads have returned. Contains workgroup barriers: call from
@@ -271,7 +271,7 @@ __device__ __forceinline__ void wg_sum(float (&v)[K], float* lds) {
     }
   }
   lds_barrier();
-  if constexpr (K < 4) {  // few values: every thread adds the wavefront totals
+  if constexpr (K <= 4) {  // few values: every thread adds the wavefront totals
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       float s = lds[k];

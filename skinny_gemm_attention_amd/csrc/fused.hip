@@ -273,15 +273,19 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
   // one token: its mixture (and mixture*gains) stay in registers; more
   // tokens park their mixtures in LDS
   float mix1[kOne ? NCH : 1][8], mg1[kOne ? NCH : 1][8];
+  float pm2[KT][NCH];  // per-chunk sums of mix^2 (the post partial that needs no new prefix)
 #pragma unroll
   for (int k = 0; k < KT; ++k) {
     pre[k] = PreScalars{0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) pm2[k][j] = 0.0f;
     if (k < ntok) {
       float mix[NCH][8];
       pre[k] = token_pre<NT, NCH>(a, o + k * NO, w, mix, lds_pre);
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int c = tid + j * NT;
+        pm2[k][j] = chunk_mix2(mix[j]);
         if (kOne) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
@@ -300,8 +304,9 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
 
   // post: collect every token's new prefix from the mailbox. Each chunk's
   // post partials (and, for one token, new*gains) are formed as soon as it
-  // arrives and its mailbox words are re-armed; only the reduction and the
-  // output remain once the last chunk is in.
+  // arrives (its mix^2 partial already in pre); once the last chunk is in,
+  // the mailbox words are re-armed and only the reduction and the output
+  // remain.
   int tok[KT];
 #pragma unroll
   for (int k = 0; k < KT; ++k) tok[k] = k < ntok ? o + k * NO : o;
@@ -316,7 +321,8 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       nbits[k][j] = u32x4{0u, 0u, 0u, 0u};
-      pc[k][j][0] = pc[k][j][1] = pc[k][j][2] = pc[k][j][3] = 0.0f;
+      pc[k][j][0] = pc[k][j][1] = pc[k][j][2] = 0.0f;
+      pc[k][j][3] = pm2[k][j];
       if (k < ntok && tid + j * NT < CH) pending |= 1u << (k * NCH + j);
     }
 #pragma unroll
@@ -344,7 +350,11 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
           } else {
             load_mix(sm.o.mix[k], c, true, mx);
           }
-          chunk_post(nw, w[j], mx, pc[k][j]);
+          float q[3];
+          chunk_post_new(nw, w[j], mx, q);
+          pc[k][j][0] = q[0];
+          pc[k][j][1] = q[1];
+          pc[k][j][2] = q[2];
         }
       }
     bits = 0;

@@ -205,11 +205,16 @@ struct GemmLds {
         red[((kp * RT + rh * RTW + rt) * TT + tt) * 64 + lane] = acc[rt][tt];
   }
 
-  // Sum over the k-partials, in k-slice order, of quad q < kQuads.
+  // Sum over the k-partials, in k-slice order, of quad q < kQuads. All NP
+  // reads are issued before the first addition (one LDS round trip).
   __device__ static __forceinline__ f32x4 gather(const f32x4* red, int q) {
-    f32x4 s = red[q];
+    f32x4 p[NP];
 #pragma unroll
-    for (int w = 1; w < NP; ++w) s += red[w * kQuads + q];
+    for (int w = 0; w < NP; ++w) p[w] = red[w * kQuads + q];
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 s = p[0];
+#pragma unroll
+    for (int w = 1; w < NP; ++w) s += p[w];
     return s;
   }
 
