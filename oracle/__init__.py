@@ -49,10 +49,13 @@ def _load():
                                                  P, I64, F, F, I, I, I, I, I, I, P, I]
         lib.oracle_attnres_oproj.argtypes = [P, I64, P, I64, I, P, I64, P, I64, I64, I, P, P, P,
                                              P, I64, P, I64, F, F, I, I, I, I, I, I, P, P, I]
+        lib.oracle_attnres_pre.argtypes = [P, I64, I64, I, P, P, F, I, I, I, P, I64, P, I]
+        lib.oracle_attnres_post.argtypes = [P, I64, P, I64, P, I64, I64, I, P, P, P, P, I64, P,
+                                            I64, P, I64, P, F, F, I, I, I, I, I, I, P, I]
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_round_bf16.restype = ctypes.c_uint16
         for f in ("oracle_gemm", "oracle_attnres", "oracle_attnres_streaming",
-                  "oracle_attnres_oproj"):
+                  "oracle_attnres_oproj", "oracle_attnres_pre", "oracle_attnres_post"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -151,3 +154,43 @@ def attnres_oproj(x, W, prefix, blocks, norm, query, out_norm, *, nb, write=-1, 
     if rc:
         raise ValueError("oracle_attnres_oproj: invalid arguments")
     return AttnResResult(out=out, prefix=prefix, blocks=blocks, aux=auxa, out_exact=oe, y=y)
+
+
+def attnres_pre(blocks, norm, query, *, nb, eps=1e-6, nthreads=1):
+    """Saved-block statistics of every token of ``blocks`` [T, cap, H]: the
+    unnormalised mixture [T, H] and (maximum, exp_sum) [T, 2], in FP64."""
+    blocks = _u16(blocks)
+    T, cap, H = blocks.shape
+    norm, query = _u16(norm), _u16(query)
+    mixture = np.zeros((T, H), np.float64)
+    scal = np.zeros((T, 2), np.float64)
+    rc = _load().oracle_attnres_pre(_p(blocks), cap * H, H, cap, _p(norm), _p(query), eps, T, H,
+                                    nb, _p(mixture), H, _p(scal), nthreads)
+    if rc:
+        raise ValueError("oracle_attnres_pre: invalid arguments")
+    return mixture, scal
+
+
+def attnres_post(delta, prefix, blocks, norm, query, out_norm, mixture, scal, *, nb, write=-1,
+                 has_delta=1, final=0, eps=1e-6, out_eps=1e-6, aux=True, nthreads=1):
+    """AttnRes post() on given saved-block statistics ``mixture`` [T, H] and
+    ``scal`` [T, 2] (any float dtype; widened exactly to FP64)."""
+    delta, prefix = _u16(delta), _u16(prefix).copy()
+    T, H = delta.shape
+    if blocks is None:
+        blocks = np.zeros((T, 1, H), np.uint16)
+    blocks = _u16(blocks).copy()
+    cap = blocks.shape[1]
+    norm, query, out_norm = _u16(norm), _u16(query), _u16(out_norm)
+    mix64 = np.ascontiguousarray(mixture, dtype=np.float64)
+    scal64 = np.ascontiguousarray(scal, dtype=np.float64)
+    out = np.zeros((T, H), np.uint16)
+    auxa = np.zeros((T, H), np.uint16) if aux else None
+    oe = np.zeros((T, H), np.float64)
+    rc = _load().oracle_attnres_post(
+        _p(delta), H, _p(prefix), H, _p(blocks), cap * H, H, cap, _p(norm), _p(query),
+        _p(out_norm), _p(out), H, _p(auxa), H, _p(mix64), H, _p(scal64), eps, out_eps, T, H, nb,
+        write, has_delta, final, _p(oe), nthreads)
+    if rc:
+        raise ValueError("oracle_attnres_post: invalid arguments")
+    return AttnResResult(out=out, prefix=prefix, blocks=blocks, aux=auxa, out_exact=oe)

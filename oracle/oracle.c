@@ -443,5 +443,164 @@ int oracle_attnres_oproj(const uint16_t* x, int64_t ldx, const uint16_t* W, int6
                         has_delta, final_boundary, NULL, out_exact, NULL, NULL, nthreads);
 }
 
+/* ---- saved-block statistics and the post step on given statistics ------------
+ * The state ClusterAttnRes carries from pre() to post() (attn_res.kernel page,
+ * method state: the mixture row and the two scalars maximum and exp_sum), which
+ * the fused o-projection also stores for the next layer's AttnRes over the same
+ * saved blocks (oproj.prepared page, PreparedOproj.bind_ahead and the `ahead`
+ * rows of compile_oproj). Plain definitions, per token t:
+ *   l_b      = (v_b . w) * rrms(sum v_b^2, eps)        b < nb, w = norm * query
+ *   m        = max_b l_b                                (0 when nb == 0)
+ *   S        = sum_b exp(l_b - m)                       (0 when nb == 0)
+ *   mix_i    = sum_b exp(l_b - m) v_b,i                 (0 when nb == 0)
+ * mixture [T, H] (row stride ld_mix) and scal [T, 2] = (m, S) are doubles. */
+typedef struct {
+  const uint16_t* blocks;
+  int64_t bst_t, bst_b;
+  const uint16_t *norm, *query;
+  double eps;
+  int H, nb;
+  double* mixture;
+  int64_t ld_mix;
+  double* scal;
+} pre_ctx;
+
+static void pre_tokens(void* p, int lo, int hi) {
+  const pre_ctx* c = (const pre_ctx*)p;
+  const int H = c->H, nb = c->nb;
+  double lg[8];
+  for (int t = lo; t < hi; ++t) {
+    double* mix = c->mixture + (int64_t)t * c->ld_mix;
+    for (int i = 0; i < H; ++i) mix[i] = 0.0;
+    for (int b = 0; b < nb; ++b) {
+      const uint16_t* row = c->blocks + t * c->bst_t + b * c->bst_b;
+      double ss = 0.0, d = 0.0;
+      for (int i = 0; i < H; ++i) {
+        double vi = bf(row[i]);
+        ss += vi * vi;
+        d += vi * (bf(c->norm[i]) * bf(c->query[i]));
+      }
+      lg[b] = d * rrms(ss, H, c->eps);
+    }
+    double m = 0.0, S = 0.0;
+    if (nb > 0) {
+      m = lg[0];
+      for (int b = 1; b < nb; ++b)
+        if (lg[b] > m) m = lg[b];
+      for (int b = 0; b < nb; ++b) {
+        const uint16_t* row = c->blocks + t * c->bst_t + b * c->bst_b;
+        double e = exp(lg[b] - m);
+        S += e;
+        for (int i = 0; i < H; ++i) mix[i] += e * bf(row[i]);
+      }
+    }
+    c->scal[2 * t] = m;
+    c->scal[2 * t + 1] = S;
+  }
+}
+
+int oracle_attnres_pre(const uint16_t* blocks, int64_t bst_t, int64_t bst_b, int cap,
+                       const uint16_t* norm, const uint16_t* query, float eps, int T, int H,
+                       int nb, double* mixture, int64_t ld_mix, double* scal, int nthreads) {
+  if (!norm || !query || !mixture || !scal || T < 0 || H < 1 || nb < 0 || nb > 8 || nb > cap ||
+      ld_mix < H || (nb > 0 && !blocks))
+    return OR_EINVAL;
+  pre_ctx c = {blocks, bst_t, bst_b, norm, query, (double)eps, H, nb, mixture, ld_mix, scal};
+  parallel_ranges(pre_tokens, &c, T, nthreads);
+  return OR_OK;
+}
+
+/* post() on given statistics (m, S, mix) of nb saved blocks, per token t:
+ *   new  = bf16(prefix + delta)  or  delta
+ *   l_n  = (new . w) * rrms(sum new^2, eps)
+ *   nb == 0: h = new (the statistics are not read)
+ *   else: top = max(m, l_n), alpha = exp(m - top), e_n = exp(l_n - top),
+ *         D = alpha S + e_n, h = (alpha mix + e_n new) / D,
+ *         rounded to bf16 at a final boundary
+ *   out  = bf16(h * rrms(sum h^2, out_eps) * out_norm)
+ *   prefix, aux and blocks[write] receive new.
+ * With (m, S, mix) from oracle_attnres_pre this is exactly the softmax over
+ * the nb blocks and the new prefix: alpha e_b / D = p_b and e_n / D = p_n. */
+typedef struct {
+  attn_ctx a;
+  const double* mixture;
+  int64_t ld_mix;
+  const double* scal;
+} post_ctx;
+
+static void post_tokens(void* p, int lo, int hi) {
+  const post_ctx* pc = (const post_ctx*)p;
+  const attn_ctx* c = &pc->a;
+  const int H = c->H, nb = c->nb;
+  double* nw = (double*)malloc(sizeof(double) * H);
+  double* h = (double*)malloc(sizeof(double) * H);
+  uint16_t* newbits = (uint16_t*)malloc(sizeof(uint16_t) * H);
+  for (int t = lo; t < hi; ++t) {
+    for (int i = 0; i < H; ++i) {
+      double d = bf(c->delta[t * c->ld_delta + i]);
+      newbits[i] = c->has_delta ? rn_bf16(bf(c->prefix[t * c->ld_prefix + i]) + d)
+                                : c->delta[t * c->ld_delta + i];
+      nw[i] = bf(newbits[i]);
+    }
+    if (nb == 0) {
+      for (int i = 0; i < H; ++i) h[i] = nw[i];
+    } else {
+      double ss = 0.0, d = 0.0;
+      for (int i = 0; i < H; ++i) {
+        ss += nw[i] * nw[i];
+        d += nw[i] * (bf(c->norm[i]) * bf(c->query[i]));
+      }
+      const double ln = d * rrms(ss, H, c->eps);
+      const double m = pc->scal[2 * t], S = pc->scal[2 * t + 1];
+      const double top = m > ln ? m : ln;
+      const double alpha = exp(m - top), en = exp(ln - top);
+      const double D = alpha * S + en;
+      const double* mix = pc->mixture + (int64_t)t * pc->ld_mix;
+      for (int i = 0; i < H; ++i) h[i] = (alpha * mix[i] + en * nw[i]) / D;
+      if (c->final)
+        for (int i = 0; i < H; ++i) h[i] = bf(rn_bf16(h[i]));
+    }
+    double hs = 0.0;
+    for (int i = 0; i < H; ++i) hs += h[i] * h[i];
+    const double s = rrms(hs, H, c->out_eps);
+    for (int i = 0; i < H; ++i) {
+      double o = h[i] * s * bf(c->out_norm[i]);
+      if (c->out_exact) c->out_exact[(int64_t)t * H + i] = o;
+      c->out[t * c->ld_out + i] = rn_bf16(o);
+    }
+    for (int i = 0; i < H; ++i) c->prefix[t * c->ld_prefix + i] = newbits[i];
+    if (c->aux)
+      for (int i = 0; i < H; ++i) c->aux[t * c->ld_aux + i] = newbits[i];
+    if (c->write >= 0)
+      for (int i = 0; i < H; ++i) c->blocks[t * c->bst_t + c->write * c->bst_b + i] = newbits[i];
+  }
+  free(nw);
+  free(h);
+  free(newbits);
+}
+
+/* Arguments as oracle_attnres, with the saved-block statistics given: mixture
+ * [T, H] (row stride ld_mix) and scal [T, 2] = (m, S), doubles (statistics a
+ * GPU stored as float32 are widened exactly by the caller). blocks is only
+ * written (slot write) and may be NULL when write == -1. */
+int oracle_attnres_post(const uint16_t* delta, int64_t ld_delta, uint16_t* prefix,
+                        int64_t ld_prefix, uint16_t* blocks, int64_t bst_t, int64_t bst_b,
+                        int cap, const uint16_t* norm, const uint16_t* query,
+                        const uint16_t* out_norm, uint16_t* out, int64_t ld_out, uint16_t* aux,
+                        int64_t ld_aux, const double* mixture, int64_t ld_mix, const double* scal,
+                        float eps, float out_eps, int T, int H, int nb, int write, int has_delta,
+                        int final_boundary, double* out_exact, int nthreads) {
+  if (!delta || !prefix || !norm || !query || !out_norm || !out || T < 0 || H < 1 || nb < 0 ||
+      nb > 8 || nb > cap || write < -1 || write >= cap || (write >= 0 && !blocks))
+    return OR_EINVAL;
+  if (nb > 0 && (!mixture || !scal || ld_mix < H)) return OR_EINVAL;
+  post_ctx c = {{delta, ld_delta, prefix, ld_prefix, blocks, bst_t, bst_b, norm, query, out_norm,
+                 out, ld_out, aux, ld_aux, (double)eps, (double)out_eps, H, nb, write,
+                 has_delta != 0, final_boundary != 0, NULL, out_exact, NULL, NULL},
+                mixture, ld_mix, scal};
+  parallel_ranges(post_tokens, &c, T, nthreads);
+  return OR_OK;
+}
+
 /* Exposed for the pins of the rounding rule. */
 uint16_t oracle_round_bf16(double z) { return rn_bf16(z); }
