@@ -154,6 +154,62 @@ int attnres_oproj_run(const void* x, int64_t ldx, const void* W, int64_t ldw, in
                       float eps, float out_eps, int M, int H, int nb, int write, int has_delta,
                       int final_boundary, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * attnres_oproj_ahead_run - attnres_oproj_run that also stores the saved-block
+ * statistics of the next layer's AttnRes over the same saved blocks
+ * (oproj.prepared page: PreparedOproj.bind_ahead, and compile_oproj's `ahead`
+ * rows; the statistics are the state ClusterAttnRes carries from pre to post
+ * on the attn_res.kernel page: the mixture row and maximum / exp_sum). With
+ * w' = next_norm * next_query and, for b < nb, the saved blocks as they are at
+ * launch (a scored slot that this call overwrites contributes its old value):
+ *   l'_b        = (blocks[t,b] . w') * r(sum blocks[t,b]^2, next_eps)
+ *   scal[t]     = (m, S):  m = max_b l'_b,  S = sum_b exp(l'_b - m)
+ *   mixture[t]  = sum_b exp(l'_b - m) blocks[t,b]
+ * in FP32 (nb == 0: m = S = 0 and mixture[t] = 0). Every other argument and
+ * every other output are those of attnres_oproj_run, bit for bit.
+ *   next_norm, next_query [H] bf16 (read); next_eps >= 0.
+ *   mixture [M, H] FP32, row stride ld_mixture >= H, a multiple of 8 (written);
+ *   scal [M, 2] FP32, 8-byte aligned (written). They must not alias any other
+ *   argument.
+ * Errors: those of attnres_oproj_run, and ATTNRES_EINVAL / ATTNRES_EALIGN for
+ * the arguments above.
+ */
+int attnres_oproj_ahead_run(const void* x, int64_t ldx, const void* W, int64_t ldw, int K,
+                            void* prefix, int64_t ld_prefix, void* blocks, int64_t blk_stride_t,
+                            int64_t blk_stride_b, int cap, const void* norm, const void* query,
+                            const void* out_norm, void* out, int64_t ld_out, void* aux,
+                            int64_t ld_aux, float eps, float out_eps, int M, int H, int nb,
+                            int write, int has_delta, int final_boundary,
+                            const void* next_norm, const void* next_query, float next_eps,
+                            float* mixture, int64_t ld_mixture, float* scal, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * attnres_post_run - attnres_run on carried saved-block statistics instead of
+ * the saved blocks (ClusterAttnRes.post on the state pre leaves; the state
+ * attnres_oproj_ahead_run stores). For every token t < T, with new and l_n as
+ * for attnres_run and (m, S) = scal[t]:
+ *   nb == 0 : h = new (mixture and scal are not read and may be NULL)
+ *   nb >  0 : top = max(m, l_n), alpha = exp(m - top), e_n = exp(l_n - top),
+ *             D = alpha S + e_n, h = (alpha mixture[t] + e_n new) / D,
+ *             rounded to bf16 when final_boundary != 0
+ *   out[t] = bf16(h * r(sum h^2, out_eps) * out_norm); the state writes of
+ *   attnres_run (prefix, aux, blocks[t, write]).
+ * Given the statistics attnres_run would form from the same blocks, norm,
+ * query and eps, the outputs equal attnres_run's bit for bit. The saved
+ * blocks are not read: blocks is written (slot write) only and may be NULL
+ * when write == -1. nb (0..8) is the number of blocks the statistics cover.
+ *   mixture [T, H] FP32, row stride ld_mixture >= H, a multiple of 8, 16-byte
+ *   aligned; scal [T, 2] FP32, 8-byte aligned (both read).
+ * Other arguments and errors as for attnres_run (nb need not be <= cap).
+ */
+int attnres_post_run(const void* delta, int64_t ld_delta, void* prefix, int64_t ld_prefix,
+                     void* blocks, int64_t blk_stride_t, int64_t blk_stride_b, int cap,
+                     const void* norm, const void* query, const void* out_norm, void* out,
+                     int64_t ld_out, void* aux, int64_t ld_aux, const float* mixture,
+                     int64_t ld_mixture, const float* scal, float eps, float out_eps, int T, int H,
+                     int nb, int write, int has_delta, int final_boundary, void* stream);
+
 /* attnres_strerror - a static, human-readable description of a return code. */
 const char* attnres_strerror(int code);
 

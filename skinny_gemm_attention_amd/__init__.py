@@ -1,8 +1,9 @@
 """Python binding of libattnres.so (argument marshalling only).
 
-The three entry points carry the names of the C ABI in ``include/attnres.h``
-and take torch tensors that live on the GPU: bfloat16 (or 16-bit integer
-views of bfloat16 bits) with contiguous rows. Every step of the computation
+The entry points carry the names of the C ABI in ``include/attnres.h`` and
+take torch tensors that live on the GPU: bfloat16 (or 16-bit integer views of
+bfloat16 bits) with contiguous rows; carried saved-block statistics are
+float32. Every step of the computation
 runs in the library's HIP kernels; this module only reads pointers, strides
 and the current stream, calls the C function and raises ``AttnResError`` on a
 non-zero return code. There is no fallback: without the built library the
@@ -37,13 +38,20 @@ _lib.attnres_oproj_workspace_init.restype = _I
 _lib.attnres_oproj_run.argtypes = [_P, _I64, _P, _I64, _I, _P, _I64, _P, _I64, _I64, _I, _P, _P,
                                    _P, _P, _I64, _P, _I64, _F, _F, _I, _I, _I, _I, _I, _I, _P,
                                    _SZ, _P]
+_lib.attnres_oproj_ahead_run.argtypes = [_P, _I64, _P, _I64, _I, _P, _I64, _P, _I64, _I64, _I,
+                                         _P, _P, _P, _P, _I64, _P, _I64, _F, _F, _I, _I, _I, _I,
+                                         _I, _I, _P, _P, _F, _P, _I64, _P, _P, _SZ, _P]
+_lib.attnres_post_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I, _P, _P, _P, _P, _I64,
+                                  _P, _I64, _P, _I64, _P, _F, _F, _I, _I, _I, _I, _I, _I, _P]
 _lib.attnres_strerror.argtypes = [_I]
 _lib.attnres_strerror.restype = ctypes.c_char_p
-for _f in (_lib.attnres_run, _lib.wsgemm_run, _lib.attnres_oproj_run):
+for _f in (_lib.attnres_run, _lib.wsgemm_run, _lib.attnres_oproj_run,
+           _lib.attnres_oproj_ahead_run, _lib.attnres_post_run):
     _f.restype = _I
 
 EXPORTS = ("attnres_run", "wsgemm_run", "attnres_oproj_run", "attnres_oproj_workspace_size",
-           "attnres_oproj_workspace_init", "attnres_strerror")
+           "attnres_oproj_workspace_init", "attnres_oproj_ahead_run", "attnres_post_run",
+           "attnres_strerror")
 
 
 class AttnResError(RuntimeError):
@@ -66,6 +74,16 @@ def _ptr(t):
         raise AttnResError(-1, "tensors must be on the GPU")
     if t.element_size() != 2:
         raise AttnResError(-1, "tensors must hold 16-bit (bfloat16) elements")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _fptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise AttnResError(-1, "tensors must be on the GPU")
+    if t.dtype != torch.float32:
+        raise AttnResError(-1, "saved-block statistics must be float32")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -155,4 +173,56 @@ def attnres_oproj_run(x, W, prefix, blocks, norm, query, out_norm, out, aux, wor
                                 _ptr(aux), _row_stride(aux), eps, out_eps, M, H, nb, write,
                                 int(has_delta), int(final_boundary), ws, wsb, _stream(stream))
     _check(rc, "attnres_oproj_run")
+    return out, prefix, blocks
+
+
+def _block_strides(blocks):
+    if blocks is None:
+        return 0, 0, 0
+    if blocks.stride(-1) != 1:
+        raise AttnResError(-1, "block rows must be contiguous")
+    return blocks.stride(0), blocks.stride(1), blocks.shape[1]
+
+
+def attnres_oproj_ahead_run(x, W, prefix, blocks, norm, query, out_norm, out, aux, workspace,
+                            next_norm, next_query, mixture, scal, *, nb, write=-1, has_delta=1,
+                            final_boundary=0, eps=1e-6, out_eps=1e-6, next_eps=1e-6,
+                            stream=None):
+    """attnres_oproj_run that also stores the saved-block statistics of the next
+    layer's AttnRes (weights next_norm * next_query, next_eps) over the same
+    saved blocks: mixture [M, H] and scal [M, 2] (maximum, exp_sum), float32."""
+    M, K = x.shape
+    H = W.shape[0]
+    bst_t, bst_b, cap = _block_strides(blocks)
+    ws = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if mixture is not None and mixture.stride(-1) != 1:
+        raise AttnResError(-1, "mixture rows must be contiguous")
+    rc = _lib.attnres_oproj_ahead_run(
+        _ptr(x), _row_stride(x), _ptr(W), _row_stride(W), K, _ptr(prefix), _row_stride(prefix),
+        _ptr(blocks), bst_t, bst_b, cap, _ptr(norm), _ptr(query), _ptr(out_norm), _ptr(out),
+        _row_stride(out), _ptr(aux), _row_stride(aux), eps, out_eps, M, H, nb, write,
+        int(has_delta), int(final_boundary), _ptr(next_norm), _ptr(next_query), next_eps,
+        _fptr(mixture), 0 if mixture is None else mixture.stride(0), _fptr(scal), ws, wsb,
+        _stream(stream))
+    _check(rc, "attnres_oproj_ahead_run")
+    return out, prefix, blocks, mixture, scal
+
+
+def attnres_post_run(delta, prefix, blocks, norm, query, out_norm, out, aux, mixture, scal, *,
+                     nb, write=-1, has_delta=1, final_boundary=0, eps=1e-6, out_eps=1e-6,
+                     stream=None):
+    """AttnRes post() on carried saved-block statistics (mixture [T, H] and scal
+    [T, 2], float32, of nb saved blocks); blocks is only written (slot write)."""
+    T, H = delta.shape
+    bst_t, bst_b, cap = _block_strides(blocks)
+    if mixture is not None and mixture.stride(-1) != 1:
+        raise AttnResError(-1, "mixture rows must be contiguous")
+    rc = _lib.attnres_post_run(
+        _ptr(delta), _row_stride(delta), _ptr(prefix), _row_stride(prefix), _ptr(blocks), bst_t,
+        bst_b, cap, _ptr(norm), _ptr(query), _ptr(out_norm), _ptr(out), _row_stride(out),
+        _ptr(aux), _row_stride(aux), _fptr(mixture), 0 if mixture is None else mixture.stride(0),
+        _fptr(scal), eps, out_eps, T, H, nb, write, int(has_delta), int(final_boundary),
+        _stream(stream))
+    _check(rc, "attnres_post_run")
     return out, prefix, blocks

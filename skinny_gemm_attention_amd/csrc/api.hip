@@ -74,7 +74,21 @@ AttnParams make_params(const void* delta, int64_t ld_delta, void* prefix, int64_
   p.write = write;
   p.has_delta = has_delta;
   p.final_b = final_boundary;
+  p.smix = nullptr;
+  p.ld_smix = 0;
+  p.sscal = nullptr;
   return p;
+}
+
+// Checks of carried saved-block statistics: mixture [T, H] FP32 with row
+// stride ld_mix, scal [T, 2] FP32. Unused (and may be NULL) when nb == 0.
+int check_stats(const void* mixture, int64_t ld_mix, const void* scal, int H, int nb) {
+  if (nb == 0) return ATTNRES_OK;
+  if (!mixture || !scal) return ATTNRES_EINVAL;
+  if (ld_mix < H) return ATTNRES_EINVAL;
+  if (!aligned16(mixture) || (reinterpret_cast<uintptr_t>(scal) & 7u)) return ATTNRES_EALIGN;
+  if (!stride8(ld_mix)) return ATTNRES_EALIGN;
+  return ATTNRES_OK;
 }
 
 // Header, one bf16 mailbox row per token, and (beyond 32 tokens) the split-K
@@ -149,13 +163,16 @@ int attnres_oproj_workspace_init(void* workspace, size_t workspace_bytes, void* 
                                                  static_cast<hipStream_t>(stream)));
 }
 
-int attnres_oproj_run(const void* x, int64_t ldx, const void* W, int64_t ldw, int K, void* prefix,
-                      int64_t ld_prefix, void* blocks, int64_t blk_stride_t,
-                      int64_t blk_stride_b, int cap, const void* norm, const void* query,
-                      const void* out_norm, void* out, int64_t ld_out, void* aux, int64_t ld_aux,
-                      float eps, float out_eps, int M, int H, int nb, int write, int has_delta,
-                      int final_boundary, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+int oproj_common(const void* x, int64_t ldx, const void* W, int64_t ldw, int K, void* prefix,
+                 int64_t ld_prefix, void* blocks, int64_t blk_stride_t, int64_t blk_stride_b,
+                 int cap, const void* norm, const void* query, const void* out_norm, void* out,
+                 int64_t ld_out, void* aux, int64_t ld_aux, float eps, float out_eps, int M, int H,
+                 int nb, int write, int has_delta, int final_boundary, void* workspace,
+                 size_t workspace_bytes, const attnres::AheadParams& ah, void* stream) {
   int rc = check_attnres(prefix, ld_prefix, blocks, blk_stride_t, blk_stride_b, cap, norm, query,
                          out_norm, out, ld_out, aux, ld_aux, eps, out_eps, M, H, nb, write,
                          has_delta, final_boundary);
@@ -184,7 +201,85 @@ int attnres_oproj_run(const void* x, int64_t ldx, const void* W, int64_t ldw, in
                                            attnres::kWorkspaceHeader + mailbox_bytes(M, H));
   p.ng = 0;
   p.k_half = 0;
+  p.ah = ah;
   return from_hip(attnres::launch_fused(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attnres_oproj_run(const void* x, int64_t ldx, const void* W, int64_t ldw, int K, void* prefix,
+                      int64_t ld_prefix, void* blocks, int64_t blk_stride_t,
+                      int64_t blk_stride_b, int cap, const void* norm, const void* query,
+                      const void* out_norm, void* out, int64_t ld_out, void* aux, int64_t ld_aux,
+                      float eps, float out_eps, int M, int H, int nb, int write, int has_delta,
+                      int final_boundary, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  attnres::AheadParams ah = {nullptr, nullptr, 0.0f, nullptr, 0, nullptr};
+  return oproj_common(x, ldx, W, ldw, K, prefix, ld_prefix, blocks, blk_stride_t, blk_stride_b,
+                      cap, norm, query, out_norm, out, ld_out, aux, ld_aux, eps, out_eps, M, H,
+                      nb, write, has_delta, final_boundary, workspace, workspace_bytes, ah,
+                      stream);
+}
+
+int attnres_oproj_ahead_run(const void* x, int64_t ldx, const void* W, int64_t ldw, int K,
+                            void* prefix, int64_t ld_prefix, void* blocks, int64_t blk_stride_t,
+                            int64_t blk_stride_b, int cap, const void* norm, const void* query,
+                            const void* out_norm, void* out, int64_t ld_out, void* aux,
+                            int64_t ld_aux, float eps, float out_eps, int M, int H, int nb,
+                            int write, int has_delta, int final_boundary,
+                            const void* next_norm, const void* next_query, float next_eps,
+                            float* mixture, int64_t ld_mixture, float* scal, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!next_norm || !next_query || !mixture || !scal) return ATTNRES_EINVAL;
+  if (!(next_eps >= 0.0f) || next_eps > 1e30f) return ATTNRES_EINVAL;
+  if (H >= 8 && H <= ATTNRES_MAX_H && !(H & 7)) {  // other H: rejected below
+    if (ld_mixture < H) return ATTNRES_EINVAL;
+  }
+  if (!aligned16(next_norm) || !aligned16(next_query) || !aligned16(mixture) ||
+      (reinterpret_cast<uintptr_t>(scal) & 7u))
+    return ATTNRES_EALIGN;
+  if (!stride8(ld_mixture)) return ATTNRES_EALIGN;
+  attnres::AheadParams ah = {static_cast<const uint16_t*>(next_norm),
+                             static_cast<const uint16_t*>(next_query), next_eps, mixture,
+                             ld_mixture, scal};
+  return oproj_common(x, ldx, W, ldw, K, prefix, ld_prefix, blocks, blk_stride_t, blk_stride_b,
+                      cap, norm, query, out_norm, out, ld_out, aux, ld_aux, eps, out_eps, M, H,
+                      nb, write, has_delta, final_boundary, workspace, workspace_bytes, ah,
+                      stream);
+}
+
+int attnres_post_run(const void* delta, int64_t ld_delta, void* prefix, int64_t ld_prefix,
+                     void* blocks, int64_t blk_stride_t, int64_t blk_stride_b, int cap,
+                     const void* norm, const void* query, const void* out_norm, void* out,
+                     int64_t ld_out, void* aux, int64_t ld_aux, const float* mixture,
+                     int64_t ld_mixture, const float* scal, float eps, float out_eps, int T, int H,
+                     int nb, int write, int has_delta, int final_boundary, void* stream) {
+  if (T < 0) return ATTNRES_EINVAL;
+  if (T == 0) return ATTNRES_OK;  // nothing to read or write
+  // the blocks are only written here: validate them as for a call that scores none
+  int rc = check_attnres(prefix, ld_prefix, blocks, blk_stride_t, blk_stride_b, cap, norm, query,
+                         out_norm, out, ld_out, aux, ld_aux, eps, out_eps, T, H, 0, write,
+                         has_delta, final_boundary);
+  if (rc) return rc;
+  if (nb < 0 || nb > ATTNRES_MAX_BLOCKS) return ATTNRES_ERANGE;
+  rc = check_stats(mixture, ld_mixture, scal, H, nb);
+  if (rc) return rc;
+  if (!delta) return ATTNRES_EINVAL;
+  if (ld_delta < H) return ATTNRES_EINVAL;
+  if (!aligned16(delta)) return ATTNRES_EALIGN;
+  if (!stride8(ld_delta)) return ATTNRES_EALIGN;
+  AttnParams p = make_params(delta, ld_delta, prefix, ld_prefix, blocks, blk_stride_t,
+                             blk_stride_b, norm, query, out_norm, out, ld_out, aux, ld_aux, eps,
+                             out_eps, T, H, nb, write, has_delta, final_boundary);
+  // nb == 0 reads no statistics: the plain kernel gives the same result
+  if (nb > 0) {
+    p.smix = mixture;
+    p.ld_smix = ld_mixture;
+    p.sscal = scal;
+  }
+  return from_hip(attnres::launch_attnres(p, static_cast<hipStream_t>(stream)));
 }
 
 const char* attnres_strerror(int code) {

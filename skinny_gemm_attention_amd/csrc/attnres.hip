@@ -5,11 +5,18 @@
 // out_norm, delta, old prefix), so one DRAM round trip covers the whole row
 // set; the two (final boundary: three) 7168-wide sums are fixed-order
 // workgroup reductions.
+//
+// STATS: post() on carried saved-block statistics (the state ClusterAttnRes
+// keeps between pre and post: the mixture row and maximum / exp_sum), as the
+// fused kernel stores them for the next layer (oproj.prepared page,
+// PreparedOproj.bind_ahead). The saved blocks are then not read; everything
+// after pre is the same code, so given the statistics that pre would have
+// formed, the results are the same bits.
 #include "launch.hpp"
 
 namespace attnres {
 
-template <int NT>
+template <int NT, bool STATS>
 __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
   constexpr int NW = TokenShape<NT>::NW, NCH = TokenShape<NT>::NCH;
   __shared__ float lds_pre[wg_sum_lds<16, NW>], lds_post[wg_sum_lds<4, NW>],
@@ -17,7 +24,7 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
   const int t = blockIdx.x, tid = threadIdx.x, CH = a.H >> 3;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  u32x4 vb[kMaxBlocks][NCH], g[NCH], d[NCH], p[NCH];
+  u32x4 vb[kMaxBlocks][NCH], g[NCH], d[NCH], p[NCH], sm[NCH][2];
   float w[NCH][8];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
@@ -26,7 +33,11 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
     const size_t col = (size_t)c * 8;
 #pragma unroll
     for (int b = 0; b < kMaxBlocks; ++b)
-      vb[b][j] = (valid && b < a.nb) ? ld16(a.blocks + t * a.bst_t + b * a.bst_b + col) : zero;
+      vb[b][j] = (!STATS && valid && b < a.nb) ? ld16(a.blocks + t * a.bst_t + b * a.bst_b + col)
+                                               : zero;
+    const bool sv = STATS && valid && a.nb > 0;
+    sm[j][0] = sv ? ld16(a.smix + t * a.ld_smix + col) : zero;
+    sm[j][1] = sv ? ld16(a.smix + t * a.ld_smix + col + 4) : zero;
     g[j] = valid ? ld16(a.out_norm + col) : zero;
     d[j] = valid ? ld16(a.delta + t * a.ld_delta + col) : zero;
     p[j] = (valid && a.has_delta) ? ld16(a.prefix + t * a.ld_prefix + col) : zero;
@@ -41,7 +52,22 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
   // pre: saved-block statistics and the unnormalised mixture
   float mix[NCH][8];
   PreScalars pre = {0.0f, 0.0f};
-  if (a.nb > 0) {
+  if (STATS) {
+    if (a.nb > 0) {
+      pre.maxl = a.sscal[2 * t];
+      pre.S = a.sscal[2 * t + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 v = __builtin_bit_cast(f32x4, sm[j][h]);
+        mix[j][4 * h] = v.x;
+        mix[j][4 * h + 1] = v.y;
+        mix[j][4 * h + 2] = v.z;
+        mix[j][4 * h + 3] = v.w;
+      }
+  } else if (a.nb > 0) {
     float ps[16];
     pre_partials(vb, w, a.nb, ps);
     wg_sum<16, NW>(ps, lds_pre);
@@ -103,7 +129,10 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
 
 hipError_t launch_attnres(const AttnParams& p, hipStream_t stream) {
   constexpr int NT = kTokenThreads;
-  hipLaunchKernelGGL((attnres_kernel<NT>), dim3(p.T), dim3(NT), 0, stream, p);
+  if (p.smix)
+    hipLaunchKernelGGL((attnres_kernel<NT, true>), dim3(p.T), dim3(NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attnres_kernel<NT, false>), dim3(p.T), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -19,6 +19,11 @@
 // are the highest workgroup ids and wait only on workgroups that never wait,
 // so the grid drains whatever the residency.
 //
+// With look-ahead statistics (fused_ahead_kernel; oproj.prepared page,
+// PreparedOproj.bind_ahead) the owners also form, from the saved blocks they
+// already hold, the pre() state of the next layer's AttnRes (its norm, query
+// and eps) and store it: mixture row and (maximum, exp_sum) per token.
+//
 // Mailbox hand-off (the sentinel scheme of the pages' Lamport mailboxes,
 // oproj.prepared page and positive_zero on the gemm.ws_gemm page): every
 // mailbox word holds the bf16 pair (+0.0, -0.0) between calls. A new-prefix
@@ -73,8 +78,8 @@ struct FusedCore<true, RT, TT> {
   using type = GemmLdsSplit<TT>;
 };
 
-template <int RT, int TT, bool SPLIT>
-__global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int R, int G, int NO) {
+template <int RT, int TT, bool SPLIT, bool AHEAD>
+__device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, int NO) {
   constexpr int NT = kTokenThreads, NW = NT / 64;
   using C = typename FusedCore<SPLIT, RT, TT>::type;
   static_assert(C::NT == NT, "one workgroup shape for both roles");
@@ -267,8 +272,9 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
   for (int k = 0; k < KT; ++k)
     if (o + k * NO < M) ntok = k + 1;
 
-  float gg[NCH][8], w[NCH][8];
+  float gg[NCH][8], w[NCH][8], w2[AHEAD ? NCH : 1][8];
   token_weights<NT, NCH>(a, w, gg);
+  if constexpr (AHEAD) pair_weights<NT, NCH>(f.ah.norm, f.ah.query, a.H, w2);
   PreScalars pre[KT];
   // one token: its mixture (and mixture*gains) stay in registers; more
   // tokens park their mixtures in LDS
@@ -280,8 +286,27 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
 #pragma unroll
     for (int j = 0; j < NCH; ++j) pm2[k][j] = 0.0f;
     if (k < ntok) {
+      const int t = o + k * NO;
       float mix[NCH][8];
-      pre[k] = token_pre<NT, NCH>(a, o + k * NO, w, mix, lds_pre);
+      if constexpr (AHEAD) {
+        // the next layer's statistics over the same (launch-time) saved
+        // blocks, stored for its post (oproj.prepared page, bind_ahead)
+        float mix2[NCH][8];
+        PreScalars pre2;
+        token_pre2<NT, NCH>(a, t, w, w2, f.ah.eps, mix, mix2, pre[k], pre2, lds_pre);
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          const int c = tid + j * NT;
+          if (c < CH) {
+            float* dst = f.ah.mix + (size_t)t * f.ah.ld_mix + (size_t)c * 8;
+            st16(dst, __builtin_bit_cast(u32x4, f32x4{mix2[j][0], mix2[j][1], mix2[j][2], mix2[j][3]}));
+            st16(dst + 4, __builtin_bit_cast(u32x4, f32x4{mix2[j][4], mix2[j][5], mix2[j][6], mix2[j][7]}));
+          }
+        }
+        if (tid == 0) st8(f.ah.scal + 2 * (size_t)t, __builtin_bit_cast(u32x2, f32x2{pre2.maxl, pre2.S}));
+      } else {
+        pre[k] = token_pre<NT, NCH>(a, t, w, mix, lds_pre);
+      }
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int c = tid + j * NT;
@@ -455,6 +480,20 @@ __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int
   }
 }
 
+// Two kernel templates over one body (rather than one kernel template with a
+// look-ahead flag): hipcc emitted the host launch stub of only one of two
+// kernel instantiations that differed in nothing but such a flag.
+template <int RT, int TT, bool SPLIT>
+__global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int R, int G, int NO) {
+  fused_body<RT, TT, SPLIT, false>(f, R, G, NO);
+}
+
+template <int RT, int TT, bool SPLIT>
+__global__ __launch_bounds__(kTokenThreads) void fused_ahead_kernel(FusedParams f, int R, int G,
+                                                                     int NO) {
+  fused_body<RT, TT, SPLIT, true>(f, R, G, NO);
+}
+
 __global__ void workspace_init_kernel(unsigned* ws, size_t words) {
   const size_t header = kWorkspaceHeader / 4;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < words;
@@ -487,8 +526,12 @@ int compute_units() {
 
 template <int RT, int TT, bool SPLIT = false>
 hipError_t go(const FusedParams& p, int R, int G, int NO, hipStream_t stream) {
-  hipLaunchKernelGGL((fused_kernel<RT, TT, SPLIT>), dim3(G + NO), dim3(kTokenThreads), 0, stream, p,
-                     R, G, NO);
+  if (p.ah.mix)
+    hipLaunchKernelGGL((fused_ahead_kernel<RT, TT, SPLIT>), dim3(G + NO), dim3(kTokenThreads), 0,
+                       stream, p, R, G, NO);
+  else
+    hipLaunchKernelGGL((fused_kernel<RT, TT, SPLIT>), dim3(G + NO), dim3(kTokenThreads), 0, stream,
+                       p, R, G, NO);
   return hipGetLastError();
 }
 

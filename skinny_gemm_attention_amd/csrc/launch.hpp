@@ -50,6 +50,7 @@ struct FusedParams {
   unsigned* partials;  // split-K hand-off (see above)
   int ng;              // split-K row groups (0: no split)
   int k_half;          // split point of K
+  AheadParams ah;      // ah.mix == nullptr: no look-ahead statistics
 };
 
 hipError_t launch_wsgemm(const GemmParams& p, hipStream_t stream);

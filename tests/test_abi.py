@@ -29,6 +29,11 @@ def lib():
     L.attnres_oproj_workspace_size.argtypes = [I, I, I]
     L.attnres_oproj_workspace_size.restype = SZ
     L.attnres_oproj_workspace_init.argtypes = [P, SZ, P]
+    L.attnres_oproj_ahead_run.argtypes = [P, I64, P, I64, I, P, I64, P, I64, I64, I, P, P, P, P,
+                                          I64, P, I64, F, F, I, I, I, I, I, I, P, P, F, P, I64, P,
+                                          P, SZ, P]
+    L.attnres_post_run.argtypes = [P, I64, P, I64, P, I64, I64, I, P, P, P, P, I64, P, I64, P, I64,
+                                   P, F, F, I, I, I, I, I, I, P]
     L.attnres_strerror.argtypes = [I]
     L.attnres_strerror.restype = ctypes.c_char_p
     return L
@@ -42,7 +47,8 @@ def declared_functions():
 def test_header_symbols_exported(lib):
     names = declared_functions()
     assert set(names) == {"attnres_run", "wsgemm_run", "attnres_oproj_workspace_size",
-                          "attnres_oproj_workspace_init", "attnres_oproj_run", "attnres_strerror"}
+                          "attnres_oproj_workspace_init", "attnres_oproj_run",
+                          "attnres_oproj_ahead_run", "attnres_post_run", "attnres_strerror"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -149,3 +155,58 @@ def call_fused(lib, **kw):
 ])
 def test_attnres_oproj_run_rejects(lib, change, code):
     assert call_fused(lib, **change) == code
+
+
+def call_ahead(lib, **kw):
+    a = attn_args()
+    a.update(x=A, ldx=8192, W=A, ldw=8192, K=8192, ws=A, wsb=256 + 4 * 7168 * 2, M=4,
+             next_norm=A, next_query=A, next_eps=1e-6, mix=A, ld_mix=H, scal=A)
+    a.update(kw)
+    return lib.attnres_oproj_ahead_run(
+        a["x"], a["ldx"], a["W"], a["ldw"], a["K"], a["prefix"], a["ld_prefix"], a["blocks"],
+        a["bst_t"], a["bst_b"], a["cap"], a["norm"], a["query"], a["out_norm"], a["out"],
+        a["ld_out"], a["aux"], a["ld_aux"], a["eps"], a["out_eps"], a["M"], a["H"], a["nb"],
+        a["write"], a["has_delta"], a["final"], a["next_norm"], a["next_query"], a["next_eps"],
+        a["mix"], a["ld_mix"], a["scal"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(next_norm=None), -1), (dict(next_query=None), -1), (dict(mix=None), -1),
+    (dict(scal=None), -1), (dict(next_eps=-1.0), -1), (dict(next_eps=float("nan")), -1),
+    (dict(ld_mix=H - 8), -1), (dict(mix=A + 8), -2), (dict(scal=A + 4), -2),
+    (dict(ld_mix=H + 4), -2), (dict(next_norm=A + 2), -2),
+    # the attnres_oproj_run checks still apply
+    (dict(M=0), -3), (dict(x=None), -1), (dict(ws=None), -5), (dict(H=100), -4),
+])
+def test_attnres_oproj_ahead_run_rejects(lib, change, code):
+    assert call_ahead(lib, **change) == code
+
+
+def call_post(lib, **kw):
+    a = attn_args()
+    a.update(mix=A, ld_mix=H, scal=A)
+    a.update(kw)
+    return lib.attnres_post_run(
+        a["delta"], a["ld_delta"], a["prefix"], a["ld_prefix"], a["blocks"], a["bst_t"],
+        a["bst_b"], a["cap"], a["norm"], a["query"], a["out_norm"], a["out"], a["ld_out"],
+        a["aux"], a["ld_aux"], a["mix"], a["ld_mix"], a["scal"], a["eps"], a["out_eps"], a["T"],
+        a["H"], a["nb"], a["write"], a["has_delta"], a["final"], a["stream"])
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(mix=None), -1), (dict(scal=None), -1), (dict(ld_mix=H - 8), -1),
+    (dict(mix=A + 8), -2), (dict(scal=A + 4), -2), (dict(ld_mix=H + 4), -2),
+    (dict(nb=9), -3), (dict(nb=-1), -3), (dict(write=9), -3),
+    (dict(delta=None), -1), (dict(T=-1), -1), (dict(H=100), -4),
+    # blocks are written only: not needed without a written slot ...
+    (dict(blocks=None, write=8), -1),
+    # ... and nb may exceed cap (the statistics stand in for the blocks):
+    # this call fails on the missing delta, not on nb > cap
+    (dict(nb=8, cap=1, write=-1, bst_t=H, delta=None), -1),
+])
+def test_attnres_post_run_rejects(lib, change, code):
+    assert call_post(lib, **change) == code
+
+
+def test_attnres_post_run_empty_is_a_noop(lib):
+    assert call_post(lib, T=0) == 0
