@@ -20,9 +20,11 @@ Protocol:
 
 Prints one JSON line. `--config` picks another fused workload (0: M=1 K=1024
 nb=1; 2: M=64 K=8192 nb=8 with a block write) for side measurements; `--config
-3` (attnres_run, T=256, nb = 0..8, final boundary) and `--config 4`
-(wsgemm_run, K=7168, N=4096, M = 1, 8, 16, 64) print one JSON line per case,
-timed the same way.
+3` (attnres_run, T=256, nb = 0..8, final boundary), `--config 4`
+(wsgemm_run, K=7168, N=4096, M = 1, 8, 16, 64) and `--config 5` (look-ahead
+statistics: attnres_oproj_ahead_run beside attnres_oproj_run on workloads 0-2,
+attnres_post_run beside attnres_run at T=256, nb=8) print one JSON line per
+case, timed the same way.
 """
 from __future__ import annotations
 
@@ -103,8 +105,9 @@ def graph_time_us(torch, step, steps, warmup):
 
 
 def side_configs(args, np, torch, sga, synth):
-    """Standalone AttnRes (T=256, nb = 0..8, final boundary) or standalone
-    GEMM (K=7168, N=4096, M = 1, 8, 16, 64): one JSON line per case."""
+    """Standalone AttnRes (T=256, nb = 0..8, final boundary), standalone GEMM
+    (K=7168, N=4096, M = 1, 8, 16, 64) or the look-ahead statistics: one JSON
+    line per case."""
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -112,6 +115,9 @@ def side_configs(args, np, torch, sga, synth):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
 
     steps = min(args.steps, 400)
+    if args.config == 5:
+        lookahead_configs(args, np, torch, sga, synth, up, steps)
+        return
     if args.config == 3:
         T = 256
         for nb in range(9):
@@ -172,12 +178,98 @@ def side_configs(args, np, torch, sga, synth):
             del Ws, ys
 
 
+def _line(metric, nbytes, us, workload, **extra):
+    d = {"metric": metric, "value": round(nbytes / us / 1e3, 1), "unit": "GB/s",
+         "us_per_call": round(us, 3), "pct_of_hbm_peak":
+         round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1), "algorithmic_bytes": nbytes,
+         "dtype": "bf16", "data": "synthetic", "config": {"workload": workload, **extra}}
+    print(json.dumps(d), flush=True)
+
+
+def lookahead_configs(args, np, torch, sga, synth, up, steps):
+    """The fused step with and without the next layer's saved-block statistics
+    (mixture [M, H] FP32 + [M, 2] written on top), and AttnRes on carried
+    statistics (reads the FP32 mixture instead of nb saved blocks) beside
+    attnres_run."""
+    dev = torch.device("cuda:0")
+    for c, cfg in WORKLOADS.items():
+        M, K, nb, cap, write = (cfg[k] for k in ("M", "K", "nb", "cap", "write"))
+        s = synth.decode_step(M, K, nb, cap=cap, write=write, seed=0)
+        nx = synth.decode_step(1, None, 0, seed=0, layer=1)
+        copy_bytes = 2 * H * K + 2 * M * K + M * 2 * H * (4 + cap) + M * H * 4
+        L = max(2, math.ceil(FOOTPRINT / copy_bytes))
+        base = dict(x=up(s.x), W=up(s.W), prefix=up(s.prefix), blocks=up(s.blocks))
+        nq = [up(s.norm), up(s.query), up(s.out_norm)]
+        nn, nqq = up(nx.norm), up(nx.query)
+        layers = []
+        for i in range(L):
+            t = {k: v.clone() for k, v in base.items()}
+            t["out"] = torch.zeros((M, H), dtype=torch.int16, device=dev)
+            t["aux"] = torch.zeros((M, H), dtype=torch.int16, device=dev)
+            t["ws"] = sga.make_workspace(M, H, nb, dev)
+            t["mix"] = torch.zeros((M, H), dtype=torch.float32, device=dev)
+            t["scal"] = torch.zeros((M, 2), dtype=torch.float32, device=dev)
+            layers.append(t)
+        torch.cuda.synchronize()
+
+        def plain(i):
+            t = layers[i % L]
+            sga.attnres_oproj_run(t["x"], t["W"], t["prefix"], t["blocks"], *nq, t["out"],
+                                  t["aux"], t["ws"], nb=nb, write=write)
+
+        def ahead(i):
+            t = layers[i % L]
+            sga.attnres_oproj_ahead_run(t["x"], t["W"], t["prefix"], t["blocks"], *nq, t["out"],
+                                        t["aux"], t["ws"], nn, nqq, t["mix"], t["scal"], nb=nb,
+                                        write=write)
+
+        base_bytes = algorithmic_bytes(M, K, nb, write, 1)
+        extra = 2 * 2 * H + M * H * 4 + M * 8  # next norm + query, mixture, scal
+        for name, fn, nbytes in (("attnres_oproj_run", plain, base_bytes),
+                                 ("attnres_oproj_ahead_run", ahead, base_bytes + extra)):
+            us = graph_time_us(torch, fn, steps, args.warmup)
+            _line(f"{name} µs/call + achieved HBM GB/s", nbytes, us,
+                  f"{name} M={M} K={K} N=H={H} nb={nb} write={write}", layer_copies=L)
+        del layers
+    T, nb = 256, 8
+    s = synth.config_inputs(3, nb=nb)
+    mix_ref = torch.zeros((T, H), dtype=torch.float32, device=dev)
+    row = 2 * H
+    L = max(2, math.ceil(FOOTPRINT / (T * row * (nb + 5))))
+    cp = []
+    for i in range(L):
+        cp.append(dict(delta=up(s.delta), prefix=up(s.prefix), blocks=up(s.blocks),
+                       out=torch.zeros((T, H), dtype=torch.int16, device=dev),
+                       aux=torch.zeros((T, H), dtype=torch.int16, device=dev),
+                       mix=mix_ref.clone().uniform_(-1, 1),
+                       scal=torch.tensor([[0.0, 3.0]] * T, dtype=torch.float32, device=dev)))
+    nq = [up(s.norm), up(s.query), up(s.out_norm)]
+    torch.cuda.synchronize()
+
+    def run(i):
+        t = cp[i % L]
+        sga.attnres_run(t["delta"], t["prefix"], t["blocks"], *nq, t["out"], t["aux"], nb=nb,
+                        final_boundary=1)
+
+    def post(i):
+        t = cp[i % L]
+        sga.attnres_post_run(t["delta"], t["prefix"], None, *nq, t["out"], t["aux"], t["mix"],
+                             t["scal"], nb=nb, final_boundary=1)
+
+    run_bytes = 3 * row + T * row * (1 + 1 + nb + 1 + 1 + 1)
+    post_bytes = 3 * row + T * row * (1 + 1 + 1 + 1 + 1) + T * (H * 4 + 8)
+    for name, fn, nbytes in (("attnres_run", run, run_bytes), ("attnres_post_run", post, post_bytes)):
+        us = graph_time_us(torch, fn, steps, args.warmup)
+        _line(f"{name} µs/call + achieved HBM GB/s", nbytes, us,
+              f"{name} T={T} H={H} nb={nb} final=1 aux=1", layer_copies=L)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1, choices=sorted(WORKLOADS) + [3, 4])
+    ap.add_argument("--config", type=int, default=1, choices=sorted(WORKLOADS) + [3, 4, 5])
     ap.add_argument("--final", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bounded host time for the oracle baseline (0 skips it)")
@@ -196,7 +288,7 @@ def main():
     import skinny_gemm_attention_amd as sga
     import synth
 
-    if args.config in (3, 4):
+    if args.config in (3, 4, 5):
         side_configs(args, np, torch, sga, synth)
         return
 

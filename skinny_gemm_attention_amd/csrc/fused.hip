@@ -290,7 +290,9 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
       float mix[NCH][8];
       if constexpr (AHEAD) {
         // the next layer's statistics over the same (launch-time) saved
-        // blocks, stored for its post (oproj.prepared page, bind_ahead)
+        // blocks, stored for its post (oproj.prepared page, bind_ahead);
+        // non-temporal stores: a later kernel reads them (normal stores cost
+        // about 2 us at 64 tokens)
         float mix2[NCH][8];
         PreScalars pre2;
         token_pre2<NT, NCH>(a, t, w, w2, f.ah.eps, mix, mix2, pre[k], pre2, lds_pre);
@@ -299,8 +301,8 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
           const int c = tid + j * NT;
           if (c < CH) {
             float* dst = f.ah.mix + (size_t)t * f.ah.ld_mix + (size_t)c * 8;
-            st16(dst, __builtin_bit_cast(u32x4, f32x4{mix2[j][0], mix2[j][1], mix2[j][2], mix2[j][3]}));
-            st16(dst + 4, __builtin_bit_cast(u32x4, f32x4{mix2[j][4], mix2[j][5], mix2[j][6], mix2[j][7]}));
+            __builtin_nontemporal_store(f32x4{mix2[j][0], mix2[j][1], mix2[j][2], mix2[j][3]}, reinterpret_cast<f32x4*>(dst));
+            __builtin_nontemporal_store(f32x4{mix2[j][4], mix2[j][5], mix2[j][6], mix2[j][7]}, reinterpret_cast<f32x4*>(dst + 4));
           }
         }
         if (tid == 0) st8(f.ah.scal + 2 * (size_t)t, __builtin_bit_cast(u32x2, f32x2{pre2.maxl, pre2.S}));
