@@ -200,7 +200,6 @@ int oproj_common(const void* x, int64_t ldx, const void* W, int64_t ldw, int K, 
   p.partials = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
                                            attnres::kWorkspaceHeader + mailbox_bytes(M, H));
   p.ng = 0;
-  p.k_half = 0;
   p.ah = ah;
   return from_hip(attnres::launch_fused(p, static_cast<hipStream_t>(stream)));
 }

@@ -38,8 +38,10 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 //     w % STEPS for the row tiles of row group w / STEPS. Either way a
 //     wavefront's partial sums run in K order, and the NP partials of an
 //     output element are added in k-slice order.
-//   * The core streams a K range [k_begin, k_begin + K) of each row, so two
-//     workgroups can split K (the caller adds their partial products).
+//   * The core streams chunks of a K range [k_begin, k_begin + K) of each row:
+//     blocks of cblock consecutive chunks, every cstride-th block, so two
+//     workgroups can split K by taking alternate blocks (the caller adds
+//     their partial products). cstride = cblock = 1 streams the whole range.
 //   * Inside a row the 16-byte pieces are stored XOR-swizzled by (row & 15):
 //     piece p of LDS row r sits at position p ^ (r & 15). An MFMA fragment
 //     read (16 rows, one piece each) then touches 16 distinct bank groups.
@@ -82,7 +84,7 @@ struct GemmLds {
   uint32_t dst[MAXSEG];     // segment offset inside a slot (wave-uniform)
   uint32_t kb[MAXSEG];      // byte offset of this lane's piece inside a chunk
   bool rv[MAXSEG];          // this lane's row exists
-  int nseg, nwseg, nC, rot, K, wave, kp, rh, r16, kq;
+  int nseg, nwseg, nC, rot, K, cs, cbk, wave, kp, rh, r16, kq;
   f32x4 acc[RTW][TT];
 
   // Chunks are consumed in the order rot, rot + 1, ..., wrapping around.
@@ -90,9 +92,12 @@ struct GemmLds {
     const int p = c + rot;
     return p >= nC ? p - nC : p;
   }
+  // Offset (in chunks, from k_begin) of this workgroup's p-th chunk: blocks
+  // of cbk consecutive chunks, every cs-th block.
+  __device__ __forceinline__ int coff(int p) const { return (p / cbk) * cbk * cs + p % cbk; }
 
   __device__ __forceinline__ void issue(int c) {
-    const uint32_t cb = (uint32_t)phys(c) * KCB;
+    const uint32_t cb = (uint32_t)coff(phys(c)) * KCB;
     lds_char* slot = ring + (c % NSLOT) * SLOT;
 #pragma unroll
     for (int i = 0; i < MAXSEG; ++i) {
@@ -108,13 +113,14 @@ struct GemmLds {
   }
 
   // Sets up this wavefront's segments for the k range [k_begin, k_begin + K_)
-  // of rows [row0, row0 + rows) and issues the first NSLOT - 1 chunks. With
-  // rot_ > 0 the chunks are taken in rotated order (workgroups that share x
-  // then read different parts of it at a time); the order is fixed per call.
+  // of rows [row0, row0 + rows) (blocks of cblock chunks, every cstride-th
+  // block) and issues the first NSLOT - 1 chunks. With rot_ > 0 the chunks
+  // are taken in rotated order (workgroups that share x then read different
+  // parts of it at a time); the order is fixed per call.
   __device__ __forceinline__ void start(const uint16_t* __restrict__ x, int64_t ldx,
                                         const uint16_t* __restrict__ W, int64_t ldw, int M,
                                         int k_begin, int K_, int row0, int rows, char* lds,
-                                        int rot_ = 0) {
+                                        int rot_ = 0, int cstride = 1, int cblock = 1) {
     const int lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     kp = wave % NP;
@@ -122,8 +128,14 @@ struct GemmLds {
     r16 = lane & 15;
     kq = lane >> 4;
     K = K_;
+    cs = cstride;
+    cbk = cblock;
     ring = (lds_char*)lds;
-    nC = (K + KE - 1) / KE;
+    {
+      const int nt = K > 0 ? (K + KE - 1) / KE : 0;  // chunks of the range
+      const int per = cbk * cs;
+      nC = (nt / per) * cbk + min(cbk, nt % per);
+    }
     rot = nC > 0 ? rot_ % nC : 0;
     const int wseg = (rows + RPI - 1) / RPI, xseg = (M + RPI - 1) / RPI;
     const int S = wseg + xseg;
@@ -157,7 +169,7 @@ struct GemmLds {
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int ks = kp * SPW + j;
-      const int k0 = phys(c) * KE + ks * 32;
+      const int k0 = coff(phys(c)) * KE + ks * 32;
       if (k0 < K) {
         const int off = 16 * ((ks * 4 + kq) ^ r16);
         u32x4 a[RTW], b[TT];

@@ -49,7 +49,6 @@ struct FusedParams {
   unsigned* mailbox;   // [M][H / 2]
   unsigned* partials;  // split-K hand-off (see above)
   int ng;              // split-K row groups (0: no split)
-  int k_half;          // split point of K
   AheadParams ah;      // ah.mix == nullptr: no look-ahead statistics
 };
 
