@@ -99,6 +99,19 @@ struct GemmLds {
   __device__ __forceinline__ void issue(int c) {
     const uint32_t cb = (uint32_t)coff(phys(c)) * KCB;
     lds_char* slot = ring + (c % NSLOT) * SLOT;
+    if (KCB < 1024 && cb + KCB <= (uint32_t)(2 * K)) {
+      // a whole chunk: every lane loads (lanes of rows past R or M read row
+      // 0 again, into LDS rows whose outputs are discarded). Measured faster
+      // with 256- and 512-byte segments, slower with 1 KiB ones.
+#pragma unroll
+      for (int i = 0; i < MAXSEG; ++i) {
+        if (i < nwseg)  // W is read once: non-temporal
+          __builtin_amdgcn_global_load_lds(gp[i] + cb, slot + dst[i], 16, 0, kCacheNT);
+        else if (i < nseg)
+          __builtin_amdgcn_global_load_lds(gp[i] + cb, slot + dst[i], 16, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < MAXSEG; ++i) {
       if (i < nseg) {
@@ -111,6 +124,7 @@ struct GemmLds {
       }
     }
   }
+
 
   // Sets up this wavefront's segments for the k range [k_begin, k_begin + K_)
   // of rows [row0, row0 + rows) (blocks of cblock chunks, every cstride-th
