@@ -21,7 +21,8 @@ Protocol:
 Prints one JSON line. `--config` picks another fused workload (0: M=1 K=1024
 nb=1; 2: M=64 K=8192 nb=8 with a block write) for side measurements; `--config
 3` (attnres_run, T=256, nb = 0..8, final boundary), `--config 4`
-(wsgemm_run, K=7168, N=4096, M = 1, 8, 16, 64) and `--config 5` (look-ahead
+(wsgemm_run, K=7168, N=4096, M = 1, 8, 16, 48, 64; beyond 32 tokens also
+wsgemm_run_ws) and `--config 5` (look-ahead
 statistics: attnres_oproj_ahead_run beside attnres_oproj_run on workloads 0-2,
 attnres_post_run beside attnres_run at T=256, nb=8) print one JSON line per
 case, timed the same way.
@@ -152,7 +153,7 @@ def side_configs(args, np, torch, sga, synth):
             del cp
     else:
         N, K = 4096, 7168
-        for M in (1, 8, 16, 64):
+        for M in (1, 8, 16, 48, 64):
             x, W = synth.gemm_inputs(M, N, K)
             nbytes = 2 * N * K + 2 * M * K + 2 * M * N
             L = max(2, math.ceil(FOOTPRINT / (2 * N * K)))
@@ -175,6 +176,17 @@ def side_configs(args, np, torch, sga, synth):
                               "data": "synthetic", "config": {
                                   "workload": f"wsgemm_run M={M} N={N} K={K}",
                                   "layer_copies": L}}), flush=True)
+            if M > 32:  # the same GEMM with a workspace: K split across workgroups
+                wss = [sga.make_gemm_workspace(M, N, dev) for _ in range(L)]
+                torch.cuda.synchronize()
+
+                def step_ws(i):
+                    sga.wsgemm_run_ws(xg, Ws[i % L], ys[i % L], wss[i % L])
+
+                us = graph_time_us(torch, step_ws, steps, args.warmup)
+                _line("wsgemm_run_ws µs/call + achieved HBM GB/s", nbytes, us,
+                      f"wsgemm_run_ws M={M} N={N} K={K}", layer_copies=L)
+                del wss
             del Ws, ys
 
 

@@ -115,6 +115,31 @@ int wsgemm_run(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, 
                int M, int N, int K, void* stream);
 
 /*
+ * wsgemm_workspace_size - bytes of device workspace wsgemm_run_ws needs for M
+ * tokens and N rows: a 256-byte header and, beyond 32 tokens, the hand-off of
+ * FP32 partial products between the workgroups that split K.
+ */
+size_t wsgemm_workspace_size(int M, int N);
+
+/*
+ * wsgemm_run_ws - wsgemm_run (same arguments, same result up to the order of
+ * the FP32 partial sums) with a caller workspace, which lets the call split K
+ * across workgroups beyond 32 tokens (gemm.ws_gemm page, module summary: a
+ * cluster of CTAs splits K and sums the parts in K order; here up to four
+ * workgroups per 64-row group, the parts added in K order by the last one).
+ * The sums are still in a fixed order: results are bitwise reproducible run
+ * to run. Up to 32 tokens it runs wsgemm_run's kernel (bit for bit).
+ *   workspace: at least wsgemm_workspace_size(M, N) bytes, 256-byte aligned,
+ *   prepared once by attnres_oproj_workspace_init (the same format); every
+ *   call leaves it prepared again, and its first 32-bit word nonzero if a
+ *   wait gave up (the safety bound of attnres_oproj_run). Calls that may run
+ *   at the same time need distinct workspaces.
+ * Errors: those of wsgemm_run, and ATTNRES_EWORKSPACE.
+ */
+int wsgemm_run_ws(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, int64_t ldy,
+                  int M, int N, int K, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attnres_oproj_workspace_size - bytes of device workspace attnres_oproj_run
  * needs for M tokens and hidden width H (nb does not change it): a 256-byte
  * header and one bf16 mailbox row per token.

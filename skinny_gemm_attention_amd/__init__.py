@@ -31,6 +31,9 @@ _P, _I64, _I, _F, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_
 _lib.attnres_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I, _P, _P, _P, _P, _I64, _P,
                              _I64, _F, _F, _I, _I, _I, _I, _I, _I, _P]
 _lib.wsgemm_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I, _I, _I, _P]
+_lib.wsgemm_workspace_size.argtypes = [_I, _I]
+_lib.wsgemm_workspace_size.restype = _SZ
+_lib.wsgemm_run_ws.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I, _I, _I, _P, _SZ, _P]
 _lib.attnres_oproj_workspace_size.argtypes = [_I, _I, _I]
 _lib.attnres_oproj_workspace_size.restype = _SZ
 _lib.attnres_oproj_workspace_init.argtypes = [_P, _SZ, _P]
@@ -45,11 +48,12 @@ _lib.attnres_post_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I, _P, _P
                                   _P, _I64, _P, _I64, _P, _F, _F, _I, _I, _I, _I, _I, _I, _P]
 _lib.attnres_strerror.argtypes = [_I]
 _lib.attnres_strerror.restype = ctypes.c_char_p
-for _f in (_lib.attnres_run, _lib.wsgemm_run, _lib.attnres_oproj_run,
+for _f in (_lib.attnres_run, _lib.wsgemm_run, _lib.wsgemm_run_ws, _lib.attnres_oproj_run,
            _lib.attnres_oproj_ahead_run, _lib.attnres_post_run):
     _f.restype = _I
 
-EXPORTS = ("attnres_run", "wsgemm_run", "attnres_oproj_run", "attnres_oproj_workspace_size",
+EXPORTS = ("attnres_run", "wsgemm_run", "wsgemm_workspace_size", "wsgemm_run_ws",
+           "attnres_oproj_run", "attnres_oproj_workspace_size",
            "attnres_oproj_workspace_init", "attnres_oproj_ahead_run", "attnres_post_run",
            "attnres_strerror")
 
@@ -112,6 +116,27 @@ def wsgemm_run(x, W, y, stream=None):
     rc = _lib.wsgemm_run(_ptr(x), _row_stride(x), _ptr(W), _row_stride(W), _ptr(y),
                          _row_stride(y), M, N, K, _stream(stream))
     _check(rc, "wsgemm_run")
+    return y
+
+
+def wsgemm_workspace_size(M: int, N: int) -> int:
+    return int(_lib.wsgemm_workspace_size(M, N))
+
+
+def make_gemm_workspace(M: int, N: int, device="cuda") -> torch.Tensor:
+    """A workspace for wsgemm_run_ws: torch allocates it, the library arms it."""
+    ws = torch.empty(wsgemm_workspace_size(M, N), dtype=torch.uint8, device=device)
+    return attnres_oproj_workspace_init(ws)
+
+
+def wsgemm_run_ws(x, W, y, workspace, stream=None):
+    """wsgemm_run with a workspace (K split across workgroups beyond 32 tokens)."""
+    M, K = x.shape
+    N = W.shape[0]
+    rc = _lib.wsgemm_run_ws(_ptr(x), _row_stride(x), _ptr(W), _row_stride(W), _ptr(y),
+                            _row_stride(y), M, N, K, ctypes.c_void_p(workspace.data_ptr()),
+                            workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "wsgemm_run_ws")
     return y
 
 

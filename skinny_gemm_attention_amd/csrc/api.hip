@@ -127,17 +127,19 @@ int attnres_run(const void* delta, int64_t ld_delta, void* prefix, int64_t ld_pr
   return from_hip(attnres::launch_attnres(p, static_cast<hipStream_t>(stream)));
 }
 
-int wsgemm_run(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, int64_t ldy,
-               int M, int N, int K, void* stream) {
-  if (M < 0 || N < 0 || K < 0) return ATTNRES_EINVAL;
-  if (M == 0) return ATTNRES_OK;  // nothing to read or write
+}  // extern "C"
+
+namespace {
+
+// Checks of wsgemm_run's arguments (M > 0); fills p.
+int check_gemm(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, int64_t ldy,
+               int M, int N, int K, attnres::GemmParams& p) {
   if (!y || (K > 0 && (!x || !W))) return ATTNRES_EINVAL;  // x, W unread when K == 0
   if (M > ATTNRES_MAX_M) return ATTNRES_ERANGE;
   if (N < 8 || (N & 7) || (K & 7)) return ATTNRES_EUNSUPPORTED;
   if (ldy < N || (K > 0 && (ldx < K || ldw < K))) return ATTNRES_EINVAL;
   if (!aligned16(y) || (K > 0 && (!aligned16(x) || !aligned16(W)))) return ATTNRES_EALIGN;
   if (!stride8(ldy) || (K > 0 && (!stride8(ldx) || !stride8(ldw)))) return ATTNRES_EALIGN;
-  attnres::GemmParams p;
   p.x = static_cast<const uint16_t*>(x);
   p.ldx = ldx;
   p.W = static_cast<const uint16_t*>(W);
@@ -147,6 +149,39 @@ int wsgemm_run(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, 
   p.M = M;
   p.N = N;
   p.K = K;
+  return ATTNRES_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wsgemm_workspace_size(int M, int N) {
+  if (M < 0 || N < 0) return 0;
+  return attnres::kWorkspaceHeader + attnres::wsgemm_split_partial_bytes(M, N);
+}
+
+int wsgemm_run_ws(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, int64_t ldy,
+                  int M, int N, int K, void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return ATTNRES_EINVAL;
+  if (M == 0) return ATTNRES_OK;  // nothing to read or write
+  attnres::GemmParams p;
+  int rc = check_gemm(x, ldx, W, ldw, y, ldy, M, N, K, p);
+  if (rc) return rc;
+  if (!workspace || workspace_bytes < wsgemm_workspace_size(M, N) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return ATTNRES_EWORKSPACE;
+  return from_hip(attnres::launch_wsgemm_ws(p, workspace, attnres::compute_units(),
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int wsgemm_run(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, int64_t ldy,
+               int M, int N, int K, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return ATTNRES_EINVAL;
+  if (M == 0) return ATTNRES_OK;  // nothing to read or write
+  attnres::GemmParams p;
+  int rc = check_gemm(x, ldx, W, ldw, y, ldy, M, N, K, p);
+  if (rc) return rc;
   return from_hip(attnres::launch_wsgemm(p, static_cast<hipStream_t>(stream)));
 }
 

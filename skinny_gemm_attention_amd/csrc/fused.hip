@@ -46,16 +46,6 @@ __device__ __forceinline__ void st4_device(void* p, unsigned v) {
   __hip_atomic_store(reinterpret_cast<unsigned*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Mailbox polling: one 16-byte device-scope (sc1) buffer load per pending
-// chunk per round, all issued back to back; a chunk that has already arrived
-// gets an offset past the end of the buffer, which the hardware answers with
-// zeros and no memory access. Every wait is bounded by kSpinLimit rounds
-// (about a second); an owner that gives up flags the workspace and finishes.
-constexpr int kSpinLimit = 1 << 20;
-constexpr unsigned kBufferOff = 0xFFFFFFF0u;  // past num_records: reads zeros
-constexpr int kBufferDword3 = 0x00020000;     // raw buffer, 32-bit data format
-constexpr int kCacheSC1 = 16;                 // buffer-load cache policy: device scope
-
 __device__ __forceinline__ void load_mix(const float* row, int c, bool valid, float (&m)[8]) {
   if (valid) {
     const f32x4* pm = reinterpret_cast<const f32x4*>(row + c * 8);
@@ -516,8 +506,7 @@ hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
-namespace {
-
+// Compute units of the current device (cached per device; 256 if unknown).
 int compute_units() {
   static int cached[64];
   int dev = 0;
@@ -530,6 +519,8 @@ int compute_units() {
   }
   return cached[dev];
 }
+
+namespace {
 
 template <int RT, int TT, bool SPLIT = false>
 hipError_t go(const FusedParams& p, int R, int G, int NO, hipStream_t stream) {

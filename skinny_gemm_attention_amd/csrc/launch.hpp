@@ -34,6 +34,26 @@ inline size_t split_partial_bytes(int M, int H) {
   return groups * quads * 16;
 }
 
+// Polling of sentinel-armed words: one 16-byte device-scope (sc1) buffer load
+// per pending piece per round, all issued back to back; a piece that has
+// already arrived gets an offset past the end of the buffer, which the
+// hardware answers with zeros and no memory access. Every wait is bounded by
+// kSpinLimit rounds (about a second); a workgroup that gives up flags the
+// workspace and finishes.
+constexpr int kSpinLimit = 1 << 20;
+constexpr unsigned kBufferOff = 0xFFFFFFF0u;  // past num_records: reads zeros
+constexpr int kBufferDword3 = 0x00020000;     // raw buffer, 32-bit data format
+constexpr int kCacheSC1 = 16;                 // buffer-load cache policy: device scope
+
+// Hand-off bytes of wsgemm_run_ws for M tokens and N rows: up to three parts
+// per 64-row group (four-way split), one 16-byte quad per MFMA output quad.
+inline size_t wsgemm_split_partial_bytes(int M, int N) {
+  if (M <= 32) return 0;
+  const size_t groups = (size_t)(N + 63) / 64;
+  const size_t quads = 4 * (size_t)((M + 15) / 16) * 64;
+  return 3 * groups * quads * 16;
+}
+
 struct FusedWorkspace {
   unsigned error;  // nonzero after an owner gave up waiting (results invalid)
 };
@@ -52,7 +72,13 @@ struct FusedParams {
   AheadParams ah;      // ah.mix == nullptr: no look-ahead statistics
 };
 
+int compute_units();
 hipError_t launch_wsgemm(const GemmParams& p, hipStream_t stream);
+// Split K over up to four workgroups per 64-row group beyond 32 tokens (when
+// the parts fit `compute_units`), else launch_wsgemm. The workspace holds the
+// 256-byte header, then the hand-off of wsgemm_split_partial_bytes(M, N).
+hipError_t launch_wsgemm_ws(const GemmParams& p, void* workspace, int compute_units,
+                            hipStream_t stream);
 hipError_t launch_attnres(const AttnParams& p, hipStream_t stream);
 hipError_t launch_fused(const FusedParams& p, hipStream_t stream);
 hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t stream);

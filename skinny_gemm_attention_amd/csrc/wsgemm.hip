@@ -29,6 +29,142 @@ __global__ __launch_bounds__(512) void wsgemm_kernel(GemmParams p, int R) {
   }
 }
 
+// Split K for more than 32 tokens (wsgemm_run_ws): S workgroups share each
+// 64-row group, workgroup q streaming the q-th contiguous part of K. Every
+// compute unit then reads 1/S of x next to its 64 rows of W, instead of all of
+// x next to 16 rows (at M = 64 x would fill four fifths of the LDS ring). Parts
+// 0 .. S-2 store their FP32 partial products in the workspace (the
+// sentinel-armed hand-off of the fused call; stored zeros are +0.0, so no
+// partial equals the sentinel) and finish; part S-1 polls them, adds the parts
+// in part order (its own last), re-arms the words, rounds and writes y 16
+// bytes at a time. Only the last part waits, and only on lower workgroup ids.
+// S (2 or 4) is a run-time argument: hipcc emitted the host launch stub of
+// only one of two kernel instantiations that differed in nothing but S.
+constexpr int kMaxSplit = 4;
+template <int TT>
+__global__ __launch_bounds__(512) void wsgemm_split_kernel(GemmParams p, unsigned* partials,
+                                                           FusedWorkspace* ws, int ng, int kpart,
+                                                           int S) {
+  using C = GemmLdsSplit<TT>;
+  static_assert(C::NT == 512, "launch bounds");
+  static_assert(C::NP * C::kQuads * 16 + 64 * kSplitRows * 2 <= C::kLdsBytes, "y tile fits");
+  constexpr int QPT = (C::kQuads + C::NT - 1) / C::NT;
+  __shared__ __attribute__((aligned(16))) char lds[C::kLdsBytes];
+  f32x4* red = reinterpret_cast<f32x4*>(lds);  // reused once the ring is drained
+  const int g = blockIdx.x, tid = threadIdx.x;
+  const int q = g / ng, rg = g - q * ng;  // part of K, row group
+  const int row0 = rg * kSplitRows;
+  const int rows = min(kSplitRows, p.N - row0);
+  const int kbeg = q * kpart;
+  const int klen = max(0, min(kpart, p.K - kbeg));
+  int qm[QPT], qr[QPT];
+  bool qv[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int qq = tid + i * C::NT;
+    qm[i] = qr[i] = 0;
+    qv[i] = false;
+    if (qq < C::kQuads) {
+      C::quad_coords(qq, qm[i], qr[i]);
+      qv[i] = qm[i] < p.M && qr[i] < rows;
+    }
+  }
+  {
+    C core;
+    core.start(p.x, p.ldx, p.W, p.ldw, p.M, kbeg, klen, row0, rows, lds, rg);
+    core.finish();
+    core.stash(red);
+  }
+  lds_barrier();
+  f32x4 s[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) s[i] = qv[i] ? C::gather(red, tid + i * C::NT) : f32x4{0.f, 0.f, 0.f, 0.f};
+  const __amdgpu_buffer_rsrc_t part =
+      __builtin_amdgcn_make_buffer_rsrc(partials, 0, (S - 1) * ng * C::kQuads * 16, kBufferDword3);
+  if (q < S - 1) {
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      if (qv[i]) {  // +0.0 for a zero, so no stored word equals the sentinel
+        u32x4 v = __builtin_bit_cast(u32x4, s[i]);
+        v.x = v.x == kMailboxSentinel ? 0u : v.x;
+        v.y = v.y == kMailboxSentinel ? 0u : v.y;
+        v.z = v.z == kMailboxSentinel ? 0u : v.z;
+        v.w = v.w == kMailboxSentinel ? 0u : v.w;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v, part, ((q * ng + rg) * C::kQuads + tid + i * C::NT) * 16, 0, kCacheSC1);
+      }
+    }
+    return;
+  }
+  // the last part: collect the others (as the fused call's owners poll)
+  unsigned pending = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxSplit - 1; ++j)
+#pragma unroll
+    for (int i = 0; i < QPT; ++i)
+      if (j < S - 1 && qv[i]) pending |= 1u << (j * QPT + i);
+  f32x4 got[kMaxSplit - 1][QPT];
+#pragma unroll
+  for (int j = 0; j < kMaxSplit - 1; ++j)
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) got[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int spin = 0; pending != 0; ++spin) {
+    u32x4 r[kMaxSplit - 1][QPT];
+#pragma unroll
+    for (int j = 0; j < kMaxSplit - 1; ++j)
+#pragma unroll
+      for (int i = 0; i < QPT; ++i) {
+        const unsigned off = (unsigned)((j * ng + rg) * C::kQuads + tid + i * C::NT) * 16u;
+        r[j][i] = __builtin_amdgcn_raw_buffer_load_b128(
+            part, (pending & (1u << (j * QPT + i))) ? off : kBufferOff, 0, kCacheSC1);
+      }
+#pragma unroll
+    for (int j = 0; j < kMaxSplit - 1; ++j)
+#pragma unroll
+      for (int i = 0; i < QPT; ++i) {
+        const unsigned bit = 1u << (j * QPT + i);
+        const u32x4 v = r[j][i];
+        if ((pending & bit) && v.x != kMailboxSentinel && v.y != kMailboxSentinel &&
+            v.z != kMailboxSentinel && v.w != kMailboxSentinel) {
+          got[j][i] = __builtin_bit_cast(f32x4, v);
+          pending &= ~bit;
+        }
+      }
+    if (pending == 0) break;
+    if (spin >= kSpinLimit) {
+      __hip_atomic_store(&ws->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  // y (rounded, -0.0 -> +0.0) of every quad into an LDS tile [token][64 rows]
+  unsigned* tile = reinterpret_cast<unsigned*>(lds + C::NP * C::kQuads * 16);
+  const u32x4 sent = {kMailboxSentinel, kMailboxSentinel, kMailboxSentinel, kMailboxSentinel};
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    if (qv[i]) {
+      f32x4 t = got[0][i];
+#pragma unroll
+      for (int j = 1; j < kMaxSplit - 1; ++j)
+        if (j < S - 1) t += got[j][i];
+      t += s[i];
+#pragma unroll
+      for (int j = 0; j < kMaxSplit - 1; ++j)
+        if (j < S - 1)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              sent, part, ((j * ng + rg) * C::kQuads + tid + i * C::NT) * 16, 0, kCacheSC1);
+      unsigned* t2 = tile + qm[i] * (kSplitRows / 2) + (qr[i] >> 1);
+      t2[0] = positive_zero(pack2(t.x, t.y));
+      t2[1] = positive_zero(pack2(t.z, t.w));
+    }
+  }
+  lds_barrier();
+  const int om = tid >> 3, oj = tid & 7;
+  if (om < p.M && 8 * oj < rows)
+    st16(p.y + (size_t)om * p.ldy + row0 + 8 * oj,
+         *reinterpret_cast<const u32x4*>(tile + om * (kSplitRows / 2) + 4 * oj));
+}
+
 template <int RT, int TT>
 static hipError_t go(const GemmParams& p, int R, hipStream_t stream) {
   const int grid = (p.N + R - 1) / R;
@@ -53,6 +189,29 @@ hipError_t launch_wsgemm(const GemmParams& p, hipStream_t stream) {
     case 3: return go<1, 3>(p, R, stream);
     default: return go<1, 4>(p, R, stream);
   }
+}
+
+template <int TT>
+static hipError_t go_split(const GemmParams& p, unsigned* partials, FusedWorkspace* ws, int ng,
+                           int S, hipStream_t stream) {
+  using C = GemmLdsSplit<TT>;
+  const int kpart = ((p.K + S - 1) / S + C::KE - 1) / C::KE * C::KE;  // whole chunks per part
+  hipLaunchKernelGGL((wsgemm_split_kernel<TT>), dim3(S * ng), dim3(C::NT), 0, stream, p, partials,
+                     ws, ng, kpart, S);
+  return hipGetLastError();
+}
+
+hipError_t launch_wsgemm_ws(const GemmParams& p, void* workspace, int compute_units,
+                            hipStream_t stream) {
+  const int tt = (p.M + 15) / 16;
+  const int ng = (p.N + kSplitRows - 1) / kSplitRows;
+  const int S = kMaxSplit * ng <= compute_units ? kMaxSplit : 2 * ng <= compute_units ? 2 : 1;
+  if (tt < 3 || S == 1 || p.K < 256) return launch_wsgemm(p, stream);
+  FusedWorkspace* ws = static_cast<FusedWorkspace*>(workspace);
+  unsigned* partials =
+      reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + kWorkspaceHeader);
+  return tt == 3 ? go_split<3>(p, partials, ws, ng, S, stream)
+                 : go_split<4>(p, partials, ws, ng, S, stream);
 }
 
 }  // namespace attnres

@@ -24,6 +24,9 @@ def lib():
     L.attnres_run.argtypes = [P, I64, P, I64, P, I64, I64, I, P, P, P, P, I64, P, I64, F, F, I, I,
                               I, I, I, I, P]
     L.wsgemm_run.argtypes = [P, I64, P, I64, P, I64, I, I, I, P]
+    L.wsgemm_workspace_size.argtypes = [I, I]
+    L.wsgemm_workspace_size.restype = SZ
+    L.wsgemm_run_ws.argtypes = [P, I64, P, I64, P, I64, I, I, I, P, SZ, P]
     L.attnres_oproj_run.argtypes = [P, I64, P, I64, I, P, I64, P, I64, I64, I, P, P, P, P, I64, P,
                                     I64, F, F, I, I, I, I, I, I, P, SZ, P]
     L.attnres_oproj_workspace_size.argtypes = [I, I, I]
@@ -46,7 +49,8 @@ def declared_functions():
 
 def test_header_symbols_exported(lib):
     names = declared_functions()
-    assert set(names) == {"attnres_run", "wsgemm_run", "attnres_oproj_workspace_size",
+    assert set(names) == {"attnres_run", "wsgemm_run", "wsgemm_workspace_size", "wsgemm_run_ws",
+                          "attnres_oproj_workspace_size",
                           "attnres_oproj_workspace_init", "attnres_oproj_run",
                           "attnres_oproj_ahead_run", "attnres_post_run", "attnres_strerror"}
     for n in names:
@@ -210,3 +214,32 @@ def test_attnres_post_run_rejects(lib, change, code):
 
 def test_attnres_post_run_empty_is_a_noop(lib):
     assert call_post(lib, T=0) == 0
+
+
+def test_wsgemm_workspace_size(lib):
+    # header, and beyond 32 tokens three parts per 64-row group of one
+    # 16-byte quad per MFMA output quad
+    assert lib.wsgemm_workspace_size(32, 4096) == 256
+    assert lib.wsgemm_workspace_size(64, 4096) == 256 + 3 * 64 * 1024 * 16
+    assert lib.wsgemm_workspace_size(33, 1000) == 256 + 3 * 16 * 768 * 16
+    assert lib.wsgemm_workspace_size(-1, 8) == 0
+
+
+def call_gemm_ws(lib, ws=A, wsb=256 + 3 * 64 * 1024 * 16, **kw):
+    a = dict(x=A, ldx=1024, W=A, ldw=1024, y=A, ldy=4096, M=64, N=4096, K=1024)
+    a.update(kw)
+    return lib.wsgemm_run_ws(a["x"], a["ldx"], a["W"], a["ldw"], a["y"], a["ldy"], a["M"],
+                             a["N"], a["K"], ws, wsb, None)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(ws=None), -5), (dict(ws=A + 16), -5), (dict(wsb=256), -5),
+    (dict(x=None), -1), (dict(M=65), -3), (dict(N=4100), -4), (dict(ldy=4088), -1),
+    (dict(x=A + 8), -2),
+])
+def test_wsgemm_run_ws_rejects(lib, change, code):
+    assert call_gemm_ws(lib, **change) == code
+
+
+def test_wsgemm_run_ws_empty_is_a_noop(lib):
+    assert call_gemm_ws(lib, M=0, ws=None) == 0

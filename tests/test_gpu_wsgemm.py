@@ -91,3 +91,60 @@ def test_wsgemm_deterministic():
     x, W = synth.gemm_inputs(64, 4096, 7168, seed=9)
     a, b = run_gemm(x, W), run_gemm(x, W)
     assert np.array_equal(a, b)
+
+
+# ---- wsgemm_run_ws: K split across workgroups beyond 32 tokens ------------------
+
+def run_gemm_ws(x, W, ws=None, ldy=None):
+    sga = lib()
+    M, K = x.shape
+    N = W.shape[0]
+    ldy = ldy or N
+    ws = sga.make_gemm_workspace(M, N, DEV) if ws is None else ws
+    yg = torch.full((M, ldy), 0x7FC1, dtype=torch.int16, device=DEV)  # NaN poison
+    sga.wsgemm_run_ws(up(x), up(W), yg[:, :N], ws)
+    torch.cuda.synchronize()
+    words = ws.cpu().numpy().view(np.uint32)
+    assert np.all(words[:64] == 0), "workspace header not zero (a wait gave up)"
+    assert np.all(words[64:] == 0x80000000), "hand-off not re-armed"
+    y = down(yg)
+    assert np.all(y[:, N:] == 0x7FC1), "wrote past N"
+    return y[:, :N]
+
+
+@pytest.mark.parametrize("M", [33, 48, 64])
+def test_wsgemm_ws_config4(M):
+    """K = 7168, N = 4096 (four-way split) beyond 32 tokens."""
+    x, W = synth.gemm_inputs(M, 4096, 7168)
+    y = run_gemm_ws(x, W)
+    ref = oracle.gemm(x, W, nthreads=16)
+    assert_bf16_close(y, ref, f"wsgemm_ws M={M}")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 7168, 8192), (40, 1000, 1000), (33, 264, 520),
+                                   (64, 8, 264), (48, 520, 24), (57, 16384, 256),
+                                   (35, 7168, 1032), (64, 4096, 8200)])
+def test_wsgemm_ws_exact_integers(M, N, K):
+    """Integer operands: every split sums exactly, so the bits equal the oracle's."""
+    xi = rng.integers(-8, 9, (M, K))
+    wi = rng.integers(-8, 9, (N, K))
+    x, W = bits_of(xi), bits_of(wi)
+    y = run_gemm_ws(x, W, ldy=N + 8)
+    assert np.array_equal(y, oracle.gemm(x, W, nthreads=16))
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_wsgemm_ws_up_to_32_tokens_is_wsgemm_run(M):
+    x, W = synth.gemm_inputs(M, 4096, 7168)
+    assert np.array_equal(run_gemm_ws(x, W), run_gemm(x, W))
+
+
+def test_wsgemm_ws_reuses_its_workspace_and_is_deterministic():
+    x, W = synth.gemm_inputs(64, 4096, 7168)
+    ws = lib().make_gemm_workspace(64, 4096, DEV)
+    a = run_gemm_ws(x, W, ws)
+    b = run_gemm_ws(x, W, ws)
+    x2, W2 = synth.gemm_inputs(40, 4096, 7168, seed=3)
+    c = run_gemm_ws(x2, W2, ws)  # fewer tokens, same workspace
+    assert np.array_equal(a, b)
+    assert_bf16_close(c, oracle.gemm(x2, W2, nthreads=16), "reused workspace")
