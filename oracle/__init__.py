@@ -52,6 +52,8 @@ def _load():
         lib.oracle_attnres_pre.argtypes = [P, I64, I64, I, P, P, F, I, I, I, P, I64, P, I]
         lib.oracle_attnres_post.argtypes = [P, I64, P, I64, P, I64, I64, I, P, P, P, P, I64, P,
                                             I64, P, I64, P, F, F, I, I, I, I, I, I, P, I]
+        lib.oracle_moe_front.argtypes = [P, I64, P, I64, I, I, I, P, I64, I, I, I, I, I]
+        lib.oracle_moe_front.restype = ctypes.c_int
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_round_bf16.restype = ctypes.c_uint16
         for f in ("oracle_gemm", "oracle_attnres", "oracle_attnres_streaming",
@@ -194,3 +196,19 @@ def attnres_post(delta, prefix, blocks, norm, query, out_norm, mixture, scal, *,
     if rc:
         raise ValueError("oracle_attnres_post: invalid arguments")
     return AttnResResult(out=out, prefix=prefix, blocks=blocks, aux=auxa, out_exact=oe)
+
+
+def moe_front(x, W, out, *, router_base, slot, base, valid, split):
+    """The MoE-front epilogue of y = x W^T into a copy of ``out`` [M, width]
+    (bf16 patterns): router rows c < valid as FP32 words at bf16 column
+    router_base + 2 (slot + c), latent rows c >= split as bf16 at column
+    base + c - split, the rows between dropped."""
+    x, W = _u16(x), _u16(W)
+    M, K = x.shape
+    N = W.shape[0]
+    out = _u16(out).copy()
+    rc = _load().oracle_moe_front(_p(x), K, _p(W), K, M, N, K, _p(out), out.shape[1], router_base,
+                                  slot, base, valid, split)
+    if rc:
+        raise ValueError("oracle_moe_front: invalid arguments")
+    return out

@@ -602,5 +602,50 @@ int oracle_attnres_post(const uint16_t* delta, int64_t ld_delta, uint16_t* prefi
   return OR_OK;
 }
 
+/* ---- the MoE-front epilogue of WsGemm ------------------------------------------
+ * gemm.ws_gemm page, WsGemm.epilogue (and the module summary): the output rows
+ * of y = x W^T are split into a router shard, padding and a latent shard.
+ * Per token m and output row c (the GEMM's column):
+ *   c <  valid          : FP32 word of y[m, c] (-0.0 stored as +0.0,
+ *                         positive_zero32) at bf16 column
+ *                         router_base + 2 (slot + c) of out row m;
+ *   valid <= c < split  : dropped;
+ *   c >= split          : bf16 of y[m, c] (-0.0 -> +0.0, positive_zero) at bf16
+ *                         column base + c - split of out row m.
+ * The FP32 word is y rounded once from its exact sum (the plain definition;
+ * the GPU's FP32 accumulation matches it exactly on integer data). out is
+ * [M, ld_out] bf16 patterns; nothing else is written. */
+static uint32_t rn_f32_bits(double z) {
+  float f = (float)z; /* IEEE conversion: round to nearest, ties to even */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return u == 0x80000000u ? 0u : u;
+}
+
+int oracle_moe_front(const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw, int M, int N,
+                     int K, uint16_t* out, int64_t ld_out, int router_base, int slot, int base,
+                     int valid, int split) {
+  if (!x || !W || !out || M < 0 || N < 0 || K < 0 || valid < 0 || valid > split || split > N)
+    return OR_EINVAL;
+  for (int m = 0; m < M; ++m) {
+    for (int c = 0; c < N; ++c) {
+      if (c >= valid && c < split) continue;
+      double s = 0.0;
+      for (int k = 0; k < K; ++k) s += bf(x[m * ldx + k]) * bf(W[c * ldw + k]);
+      if (c < valid) {
+        const uint32_t u = rn_f32_bits(s);
+        const int64_t col = (int64_t)router_base + 2 * ((int64_t)slot + c);
+        out[m * ld_out + col] = (uint16_t)(u & 0xFFFF); /* little-endian word */
+        out[m * ld_out + col + 1] = (uint16_t)(u >> 16);
+      } else {
+        uint16_t r = rn_bf16(s);
+        if (r == 0x8000) r = 0;
+        out[m * ld_out + base + (c - split)] = r;
+      }
+    }
+  }
+  return OR_OK;
+}
+
 /* Exposed for the pins of the rounding rule. */
 uint16_t oracle_round_bf16(double z) { return rn_bf16(z); }
