@@ -22,7 +22,8 @@ Prints one JSON line. `--config` picks another fused workload (0: M=1 K=1024
 nb=1; 2: M=64 K=8192 nb=8 with a block write) for side measurements; `--config
 3` (attnres_run, T=256, nb = 0..8, final boundary), `--config 4`
 (wsgemm_run, K=7168, N=4096, M = 1, 8, 16, 48, 64; beyond 32 tokens also
-wsgemm_run_ws) and `--config 5` (look-ahead
+wsgemm_run_ws, at M = 8 and 64 also the MoE-front epilogue) and `--config 5`
+(look-ahead
 statistics: attnres_oproj_ahead_run beside attnres_oproj_run on workloads 0-2,
 attnres_post_run beside attnres_run at T=256, nb=8) print one JSON line per
 case, timed the same way.
@@ -176,6 +177,21 @@ def side_configs(args, np, torch, sga, synth):
                               "data": "synthetic", "config": {
                                   "workload": f"wsgemm_run M={M} N={N} K={K}",
                                   "layer_copies": L}}), flush=True)
+            if M in (8, 64):  # the same GEMM with the MoE-front epilogue
+                valid, split, width = 384, 512, 7168
+                mbytes = 2 * N * K + 2 * M * K + M * (4 * valid + 2 * (N - split))
+                outs = [torch.zeros((M, width), dtype=torch.int16, device=dev) for _ in range(L)]
+                torch.cuda.synchronize()
+
+                def step_moe(i):
+                    sga.wsgemm_moe_front_run(xg, Ws[i % L], outs[i % L], router_base=3584,
+                                             slot=0, base=0, valid=valid, split=split)
+
+                us = graph_time_us(torch, step_moe, steps, args.warmup)
+                _line("wsgemm_moe_front_run µs/call + achieved HBM GB/s", mbytes, us,
+                      f"wsgemm_moe_front_run M={M} N={N} K={K} valid={valid} split={split} "
+                      f"router_base=3584 base=0", layer_copies=L)
+                del outs
             if M > 32:  # the same GEMM with a workspace: K split across workgroups
                 wss = [sga.make_gemm_workspace(M, N, dev) for _ in range(L)]
                 torch.cuda.synchronize()

@@ -115,6 +115,30 @@ int wsgemm_run(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, 
                int M, int N, int K, void* stream);
 
 /*
+ * wsgemm_moe_front_run - wsgemm_run with WsGemm's MoE-front epilogue
+ * (gemm.ws_gemm page: module summary and WsGemm.epilogue): the N output rows
+ * of y = x W^T are a router shard, padding and a latent shard, written into
+ * out [M, ld_out] (bf16 patterns; the pages' [capacity, width] mailbox rows):
+ *   c <  valid          : the FP32 word of y[m, c] (FP32 accumulation, -0.0
+ *                         stored as +0.0) at bf16 columns
+ *                         router_base + 2 (slot + c) and + 1 (low half first);
+ *   valid <= c < split  : not written (padding);
+ *   c >= split          : bf16(y[m, c]) (-0.0 -> +0.0) at column base + c - split.
+ * Nothing else in out is written.
+ *   x [M, K], W [N, K] as for wsgemm_run (0 <= M <= 64, N % 8 == 0, K % 8 == 0);
+ *   out: 16-byte aligned, ld_out a multiple of 8 (any width, may be < N);
+ *   0 <= valid <= split <= N, valid and split multiples of 8; router_base and
+ *   base even and >= 0, slot >= 0; router_base + 2 (slot + valid) <= ld_out
+ *   when valid > 0 and base + N - split <= ld_out when split < N; the two
+ *   shards' column ranges must not overlap.
+ * Errors: those of wsgemm_run; ATTNRES_ERANGE for offsets outside the row,
+ * ATTNRES_EALIGN for valid / split / router_base / base off their multiples.
+ */
+int wsgemm_moe_front_run(const void* x, int64_t ldx, const void* W, int64_t ldw, void* out,
+                         int64_t ld_out, int M, int N, int K, int router_base, int slot, int base,
+                         int valid, int split, void* stream);
+
+/*
  * wsgemm_workspace_size - bytes of device workspace wsgemm_run_ws needs for M
  * tokens and N rows: a 256-byte header and, beyond 32 tokens, the hand-off of
  * FP32 partial products between the workgroups that split K.

@@ -31,6 +31,8 @@ _P, _I64, _I, _F, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_
 _lib.attnres_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I, _P, _P, _P, _P, _I64, _P,
                              _I64, _F, _F, _I, _I, _I, _I, _I, _I, _P]
 _lib.wsgemm_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I, _I, _I, _P]
+_lib.wsgemm_moe_front_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I, _I, _I, _I, _I, _I, _I,
+                                      _I, _P]
 _lib.wsgemm_workspace_size.argtypes = [_I, _I]
 _lib.wsgemm_workspace_size.restype = _SZ
 _lib.wsgemm_run_ws.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I, _I, _I, _P, _SZ, _P]
@@ -48,11 +50,13 @@ _lib.attnres_post_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I, _P, _P
                                   _P, _I64, _P, _I64, _P, _F, _F, _I, _I, _I, _I, _I, _I, _P]
 _lib.attnres_strerror.argtypes = [_I]
 _lib.attnres_strerror.restype = ctypes.c_char_p
-for _f in (_lib.attnres_run, _lib.wsgemm_run, _lib.wsgemm_run_ws, _lib.attnres_oproj_run,
+for _f in (_lib.attnres_run, _lib.wsgemm_run, _lib.wsgemm_run_ws, _lib.wsgemm_moe_front_run,
+           _lib.attnres_oproj_run,
            _lib.attnres_oproj_ahead_run, _lib.attnres_post_run):
     _f.restype = _I
 
-EXPORTS = ("attnres_run", "wsgemm_run", "wsgemm_workspace_size", "wsgemm_run_ws",
+EXPORTS = ("attnres_run", "wsgemm_run", "wsgemm_moe_front_run", "wsgemm_workspace_size",
+           "wsgemm_run_ws",
            "attnres_oproj_run", "attnres_oproj_workspace_size",
            "attnres_oproj_workspace_init", "attnres_oproj_ahead_run", "attnres_post_run",
            "attnres_strerror")
@@ -117,6 +121,19 @@ def wsgemm_run(x, W, y, stream=None):
                          _row_stride(y), M, N, K, _stream(stream))
     _check(rc, "wsgemm_run")
     return y
+
+
+def wsgemm_moe_front_run(x, W, out, *, router_base, slot, base, valid, split, stream=None):
+    """y = x W^T with the MoE-front epilogue into out [M, width] (bf16 patterns):
+    rows c < valid as FP32 words at bf16 column router_base + 2 (slot + c), rows
+    c >= split as bf16 at column base + c - split, the rows between dropped."""
+    M, K = x.shape
+    N = W.shape[0]
+    rc = _lib.wsgemm_moe_front_run(_ptr(x), _row_stride(x), _ptr(W), _row_stride(W), _ptr(out),
+                                   _row_stride(out), M, N, K, router_base, slot, base, valid,
+                                   split, _stream(stream))
+    _check(rc, "wsgemm_moe_front_run")
+    return out
 
 
 def wsgemm_workspace_size(M: int, N: int) -> int:

@@ -131,13 +131,14 @@ int attnres_run(const void* delta, int64_t ld_delta, void* prefix, int64_t ld_pr
 
 namespace {
 
-// Checks of wsgemm_run's arguments (M > 0); fills p.
+// Checks of wsgemm_run's arguments (M > 0); fills p. y rows hold N elements
+// unless `any_width` (the MoE-front epilogue checks its own columns).
 int check_gemm(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, int64_t ldy,
-               int M, int N, int K, attnres::GemmParams& p) {
+               int M, int N, int K, attnres::GemmParams& p, bool any_width = false) {
   if (!y || (K > 0 && (!x || !W))) return ATTNRES_EINVAL;  // x, W unread when K == 0
   if (M > ATTNRES_MAX_M) return ATTNRES_ERANGE;
   if (N < 8 || (N & 7) || (K & 7)) return ATTNRES_EUNSUPPORTED;
-  if (ldy < N || (K > 0 && (ldx < K || ldw < K))) return ATTNRES_EINVAL;
+  if ((!any_width && ldy < N) || ldy < 0 || (K > 0 && (ldx < K || ldw < K))) return ATTNRES_EINVAL;
   if (!aligned16(y) || (K > 0 && (!aligned16(x) || !aligned16(W)))) return ATTNRES_EALIGN;
   if (!stride8(ldy) || (K > 0 && (!stride8(ldx) || !stride8(ldw)))) return ATTNRES_EALIGN;
   p.x = static_cast<const uint16_t*>(x);
@@ -149,6 +150,7 @@ int check_gemm(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, 
   p.M = M;
   p.N = N;
   p.K = K;
+  p.moe = p.router_base = p.slot = p.base = p.valid = p.split = 0;
   return ATTNRES_OK;
 }
 
@@ -173,6 +175,33 @@ int wsgemm_run_ws(const void* x, int64_t ldx, const void* W, int64_t ldw, void* 
     return ATTNRES_EWORKSPACE;
   return from_hip(attnres::launch_wsgemm_ws(p, workspace, attnres::compute_units(),
                                             static_cast<hipStream_t>(stream)));
+}
+
+int wsgemm_moe_front_run(const void* x, int64_t ldx, const void* W, int64_t ldw, void* out,
+                         int64_t ld_out, int M, int N, int K, int router_base, int slot, int base,
+                         int valid, int split, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return ATTNRES_EINVAL;
+  if (M == 0) return ATTNRES_OK;  // nothing to read or write
+  attnres::GemmParams p;
+  int rc = check_gemm(x, ldx, W, ldw, out, ld_out, M, N, K, p, true);
+  if (rc) return rc;
+  if (router_base < 0 || slot < 0 || base < 0 || valid < 0 || split < valid || split > N)
+    return ATTNRES_ERANGE;
+  if ((valid & 7) || (split & 7) || (router_base & 1) || (base & 1)) return ATTNRES_EALIGN;
+  if (valid > 0 && (int64_t)router_base + 2 * ((int64_t)slot + valid) > ld_out) return ATTNRES_ERANGE;
+  if (split < N && (int64_t)base + (N - split) > ld_out) return ATTNRES_ERANGE;
+  if (valid > 0 && split < N) {  // the two shards must not overlap
+    const int64_t r0 = (int64_t)router_base + 2 * (int64_t)slot, r1 = r0 + 2 * (int64_t)valid;
+    const int64_t l0 = base, l1 = (int64_t)base + (N - split);
+    if (r0 < l1 && l0 < r1) return ATTNRES_ERANGE;
+  }
+  p.moe = 1;
+  p.router_base = router_base;
+  p.slot = slot;
+  p.base = base;
+  p.valid = valid;
+  p.split = split;
+  return from_hip(attnres::launch_wsgemm(p, static_cast<hipStream_t>(stream)));
 }
 
 int wsgemm_run(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, int64_t ldy,

@@ -13,6 +13,10 @@ struct GemmParams {
   uint16_t* y;
   int64_t ldy;
   int M, N, K;
+  // MoE-front epilogue (moe != 0): y rows are out rows of width ldy; output
+  // row c < valid goes as an FP32 word to bf16 column router_base + 2 (slot + c),
+  // c >= split as bf16 to column base + c - split, the rows between nowhere
+  int moe, router_base, slot, base, valid, split;
 };
 
 // Workspace of the fused kernel: a small header, then the new-prefix mailbox

@@ -1,5 +1,7 @@
 // Standalone weight-stationary skinny GEMM (vLLM gemm.ws_gemm page, WsGemm):
-// y = bf16(x W^T) with -0.0 stored as +0.0 (positive_zero).
+// y = bf16(x W^T) with -0.0 stored as +0.0 (positive_zero); optionally with
+// the MoE-front epilogue of WsGemm.epilogue (router rows as FP32 words,
+// latent rows as bf16, the padding rows between dropped).
 #include "gemm.hpp"
 #include "launch.hpp"
 
@@ -24,7 +26,24 @@ __global__ __launch_bounds__(512) void wsgemm_kernel(GemmParams p, int R) {
     if (m < p.M && r < rows) {
       const f32x4 s = C::gather(red, q);
       const u32x2 v = {positive_zero(pack2(s.x, s.y)), positive_zero(pack2(s.z, s.w))};
-      store_quad_pairs(p.y + (size_t)m * p.ldy + row0, r, rows, v);
+      if (!p.moe) {
+        store_quad_pairs(p.y + (size_t)m * p.ldy + row0, r, rows, v);
+      } else {
+        // valid and split are multiples of 8 and a quad's four rows start at
+        // a multiple of 4: the whole quad falls in one shard
+        const int c = row0 + r;
+        uint16_t* orow = p.y + (size_t)m * p.ldy;
+        if (c < p.valid) {  // router shard: FP32 words, -0.0 stored as +0.0
+          unsigned* dst = reinterpret_cast<unsigned*>(orow + p.router_base + 2 * (p.slot + c));
+          const u32x4 w = __builtin_bit_cast(u32x4, s);
+          __builtin_nontemporal_store(w.x == kMailboxSentinel ? 0u : w.x, dst);
+          __builtin_nontemporal_store(w.y == kMailboxSentinel ? 0u : w.y, dst + 1);
+          __builtin_nontemporal_store(w.z == kMailboxSentinel ? 0u : w.z, dst + 2);
+          __builtin_nontemporal_store(w.w == kMailboxSentinel ? 0u : w.w, dst + 3);
+        } else if (c >= p.split) {  // latent shard: bf16 at base + c - split
+          store_quad_pairs(orow + p.base + (row0 - p.split), r, rows, v);
+        }
+      }
     }
   }
 }

@@ -24,6 +24,7 @@ def lib():
     L.attnres_run.argtypes = [P, I64, P, I64, P, I64, I64, I, P, P, P, P, I64, P, I64, F, F, I, I,
                               I, I, I, I, P]
     L.wsgemm_run.argtypes = [P, I64, P, I64, P, I64, I, I, I, P]
+    L.wsgemm_moe_front_run.argtypes = [P, I64, P, I64, P, I64, I, I, I, I, I, I, I, I, P]
     L.wsgemm_workspace_size.argtypes = [I, I]
     L.wsgemm_workspace_size.restype = SZ
     L.wsgemm_run_ws.argtypes = [P, I64, P, I64, P, I64, I, I, I, P, SZ, P]
@@ -50,6 +51,7 @@ def declared_functions():
 def test_header_symbols_exported(lib):
     names = declared_functions()
     assert set(names) == {"attnres_run", "wsgemm_run", "wsgemm_workspace_size", "wsgemm_run_ws",
+                          "wsgemm_moe_front_run",
                           "attnres_oproj_workspace_size",
                           "attnres_oproj_workspace_init", "attnres_oproj_run",
                           "attnres_oproj_ahead_run", "attnres_post_run", "attnres_strerror"}
@@ -243,3 +245,27 @@ def test_wsgemm_run_ws_rejects(lib, change, code):
 
 def test_wsgemm_run_ws_empty_is_a_noop(lib):
     assert call_gemm_ws(lib, M=0, ws=None) == 0
+
+
+def call_moe(lib, **kw):
+    a = dict(x=A, ldx=1024, W=A, ldw=1024, out=A, ld_out=7168, M=8, N=4096, K=1024,
+             router_base=3584, slot=0, base=0, valid=384, split=512)
+    a.update(kw)
+    return lib.wsgemm_moe_front_run(a["x"], a["ldx"], a["W"], a["ldw"], a["out"], a["ld_out"],
+                                    a["M"], a["N"], a["K"], a["router_base"], a["slot"],
+                                    a["base"], a["valid"], a["split"], None)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(valid=520), -3), (dict(split=4104), -3), (dict(split=376), -3), (dict(slot=-1), -3),
+    (dict(valid=380), -2), (dict(split=516), -2), (dict(router_base=3585), -2),
+    (dict(base=3), -2), (dict(slot=1600), -3), (dict(base=3600), -3),
+    (dict(base=100), -3),  # latent columns 100..3683 would overlap the router words
+    (dict(out=None), -1), (dict(M=65), -3), (dict(out=A + 8), -2), (dict(ld_out=7164), -2),
+])
+def test_wsgemm_moe_front_run_rejects(lib, change, code):
+    assert call_moe(lib, **change) == code
+
+
+def test_wsgemm_moe_front_run_empty_is_a_noop(lib):
+    assert call_moe(lib, M=0) == 0
