@@ -23,10 +23,9 @@ nb=1; 2: M=64 K=8192 nb=8 with a block write) for side measurements; `--config
 3` (attnres_run, T=256, nb = 0..8, final boundary), `--config 4`
 (wsgemm_run, K=7168, N=4096, M = 1, 8, 16, 48, 64; beyond 32 tokens also
 wsgemm_run_ws, at M = 8 and 64 also the MoE-front epilogue) and `--config 5`
-(look-ahead
-statistics: attnres_oproj_ahead_run beside attnres_oproj_run on workloads 0-2,
-attnres_post_run beside attnres_run at T=256, nb=8) print one JSON line per
-case, timed the same way.
+(look-ahead statistics: attnres_oproj_ahead_run beside attnres_oproj_run on
+workloads 0-2, attnres_post_run beside attnres_run at T=256, nb=8) print one
+JSON line per case, timed the same way.
 """
 from __future__ import annotations
 
