@@ -45,11 +45,12 @@ FOOTPRINT = 640e6
 # HBM bytes per launch of the fused kernel from two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE; each scaled by what the counter reads for a plain
 # device copy of known size, run with --calibrate-copy-mb). A figure holds only
-# for the kernel sources it was measured on: `digest` is their SHA-256, and
-# roofline.traffic is null when the sources differ.
+# for the kernel sources it was measured on: `digest` is the SHA-256 of their
+# code (comments and whitespace aside), and roofline.traffic is null when the
+# sources differ.
 KERNEL_SOURCES = ("common.hpp", "token.hpp", "gemm.hpp", "launch.hpp", "fused.hip")
 MEASURED_TRAFFIC = {
-    1: {"digest": "01838fd78ef1c4ef486c6225cb706c06e167f26f674af6d8b90313a76c96a337", "fetch": 60990000, "write": 1102000},
+    1: {"digest": "d157f00e9a1ca1551f85b6e57892c386bf657c5dad8a51994ad728c86cc7cdf9", "fetch": 60990000, "write": 1102000},
 }
 
 WORKLOADS = {
@@ -69,13 +70,23 @@ def algorithmic_bytes(M, K, nb, write, has_delta, aux=1, H=H):
         has_delta + nb + 1 + aux + (1 if write >= 0 else 0) + 1)
 
 
+def code_text(src: str) -> str:
+    """Source text without comments and with whitespace collapsed: what the
+    compiler sees (a comment edit does not change the kernel)."""
+    import re
+
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_digest() -> str:
     import hashlib
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "skinny_gemm_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "skinny_gemm_attention_amd", "csrc", f)) as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()
 
 

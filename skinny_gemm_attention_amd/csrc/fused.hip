@@ -164,7 +164,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
         }
         return;
       }
-      // the first half's partials: poll (as the owners poll the mailbox),
+      // the first workgroup's partials: poll (as the owners poll the mailbox),
       // add, re-arm
       unsigned pending = 0;
 #pragma unroll

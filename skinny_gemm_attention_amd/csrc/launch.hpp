@@ -21,8 +21,9 @@ struct GemmParams {
 
 // Workspace of the fused kernel: a small header, then the new-prefix mailbox
 // [M][H/2] 32-bit words (a bf16 pair each), then (beyond 32 tokens) the
-// split-K hand-off: per 64-row group, the first K half's FP32 partial
-// products, one 16-byte quad per MFMA output quad. Every word after the header
+// split-K hand-off: per 64-row group, the FP32 partial products of the
+// workgroup that streams the even 4 KB blocks of K, one 16-byte quad per MFMA
+// output quad. Every word after the header
 // holds the sentinel between calls; a producer overwrites it and the consumer
 // re-arms it after reading. 0x80000000 is the bf16 pair (+0.0, -0.0), which a
 // new-prefix pair never holds, and the FP32 -0.0, which a stored partial
