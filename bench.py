@@ -22,7 +22,8 @@ Prints one JSON line. `--config` picks another fused workload (0: M=1 K=1024
 nb=1; 2: M=64 K=8192 nb=8 with a block write) for side measurements; `--config
 3` (attnres_run, T=256, nb = 0..8, final boundary), `--config 4`
 (wsgemm_run, K=7168, N=4096, M = 1, 8, 16, 48, 64; beyond 32 tokens also
-wsgemm_run_ws, at M = 8 and 64 also the MoE-front epilogue) and `--config 5`
+wsgemm_run_ws, which alone takes M = 128; at M = 8 and 64 also the MoE-front
+epilogue) and `--config 5`
 (look-ahead statistics: attnres_oproj_ahead_run beside attnres_oproj_run on
 workloads 0-2, attnres_post_run beside attnres_run at T=256, nb=8) print one
 JSON line per case, timed the same way.
@@ -164,7 +165,7 @@ def side_configs(args, np, torch, sga, synth):
             del cp
     else:
         N, K = 4096, 7168
-        for M in (1, 8, 16, 48, 64):
+        for M in (1, 8, 16, 48, 64, 128):
             x, W = synth.gemm_inputs(M, N, K)
             nbytes = 2 * N * K + 2 * M * K + 2 * M * N
             L = max(2, math.ceil(FOOTPRINT / (2 * N * K)))
@@ -178,15 +179,10 @@ def side_configs(args, np, torch, sga, synth):
             def step(i):
                 sga.wsgemm_run(xg, Ws[i % L], ys[i % L])
 
-            us = graph_time_us(torch, step, steps, args.warmup)
-            print(json.dumps({"metric": "wsgemm_run µs/call + achieved HBM GB/s",
-                              "value": round(nbytes / us / 1e3, 1), "unit": "GB/s",
-                              "us_per_call": round(us, 3), "pct_of_hbm_peak":
-                              round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1),
-                              "algorithmic_bytes": nbytes, "dtype": "bf16",
-                              "data": "synthetic", "config": {
-                                  "workload": f"wsgemm_run M={M} N={N} K={K}",
-                                  "layer_copies": L}}), flush=True)
+            if M <= 64:  # beyond 64 tokens only the workspace call takes them
+                us = graph_time_us(torch, step, steps, args.warmup)
+                _line("wsgemm_run µs/call + achieved HBM GB/s", nbytes, us,
+                      f"wsgemm_run M={M} N={N} K={K}", layer_copies=L)
             if M in (8, 64):  # the same GEMM with the MoE-front epilogue
                 valid, split, width = 384, 512, 7168
                 mbytes = 2 * N * K + 2 * M * K + M * (4 * valid + 2 * (N - split))

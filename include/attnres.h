@@ -55,6 +55,7 @@ extern "C" {
 /* Limits. */
 #define ATTNRES_MAX_BLOCKS 8 /* saved blocks scored per token (nb) */
 #define ATTNRES_MAX_M 64     /* tokens per GEMM or fused call */
+#define ATTNRES_MAX_M_WS 128 /* tokens per wsgemm_run_ws call */
 #define ATTNRES_MAX_H 8192   /* hidden width of the AttnRes paths */
 
 /*
@@ -152,7 +153,11 @@ size_t wsgemm_workspace_size(int M, int N);
  * cluster of CTAs splits K and sums the parts in K order; here up to four
  * workgroups per 64-row group, the parts added in K order by the last one).
  * The sums are still in a fixed order: results are bitwise reproducible run
- * to run. Up to 32 tokens it runs wsgemm_run's kernel (bit for bit).
+ * to run. Up to 32 tokens it runs wsgemm_run's kernel (bit for bit). It takes
+ * up to ATTNRES_MAX_M_WS tokens in one pass over W (the pages stream token
+ * groups for the same purpose); beyond 64 tokens the split is required:
+ * K >= 256 and 2 * ceil(N / 64) <= the device's compute units, else
+ * ATTNRES_EUNSUPPORTED.
  *   workspace: at least wsgemm_workspace_size(M, N) bytes, 256-byte aligned,
  *   prepared once by attnres_oproj_workspace_init (the same format); every
  *   call leaves it prepared again, and its first 32-bit word nonzero if a

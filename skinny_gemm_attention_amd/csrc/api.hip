@@ -134,9 +134,10 @@ namespace {
 // Checks of wsgemm_run's arguments (M > 0); fills p. y rows hold N elements
 // unless `any_width` (the MoE-front epilogue checks its own columns).
 int check_gemm(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, int64_t ldy,
-               int M, int N, int K, attnres::GemmParams& p, bool any_width = false) {
+               int M, int N, int K, attnres::GemmParams& p, bool any_width = false,
+               int max_m = ATTNRES_MAX_M) {
   if (!y || (K > 0 && (!x || !W))) return ATTNRES_EINVAL;  // x, W unread when K == 0
-  if (M > ATTNRES_MAX_M) return ATTNRES_ERANGE;
+  if (M > max_m) return ATTNRES_ERANGE;
   if (N < 8 || (N & 7) || (K & 7)) return ATTNRES_EUNSUPPORTED;
   if ((!any_width && ldy < N) || ldy < 0 || (K > 0 && (ldx < K || ldw < K))) return ATTNRES_EINVAL;
   if (!aligned16(y) || (K > 0 && (!aligned16(x) || !aligned16(W)))) return ATTNRES_EALIGN;
@@ -168,8 +169,10 @@ int wsgemm_run_ws(const void* x, int64_t ldx, const void* W, int64_t ldw, void* 
   if (M < 0 || N < 0 || K < 0) return ATTNRES_EINVAL;
   if (M == 0) return ATTNRES_OK;  // nothing to read or write
   attnres::GemmParams p;
-  int rc = check_gemm(x, ldx, W, ldw, y, ldy, M, N, K, p);
+  int rc = check_gemm(x, ldx, W, ldw, y, ldy, M, N, K, p, false, ATTNRES_MAX_M_WS);
   if (rc) return rc;
+  if (M > ATTNRES_MAX_M && !attnres::wsgemm_ws_splits(M, N, K, attnres::compute_units()))
+    return ATTNRES_EUNSUPPORTED;  // beyond 64 tokens only the split kernel serves
   if (!workspace || workspace_bytes < wsgemm_workspace_size(M, N) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return ATTNRES_EWORKSPACE;

@@ -265,7 +265,7 @@ using GemmLdsFor = GemmLds<RT, TT, (TT == 1 && RT == 1 ? 1024 : 512),
 // split into four k-steps by two row groups.
 constexpr int kSplitRows = 64;
 template <int TT>
-using GemmLdsSplit = GemmLds<4, TT, 256, 4>;
+using GemmLdsSplit = GemmLds<4, TT, 256, (TT <= 4 ? 4 : 3)>;  // three slots beyond 64 tokens
 
 // Rows of W per workgroup for N output rows: spread N over 256 workgroups (one
 // per compute unit), a multiple of 4, at most 32 (two 16-row MFMA tiles).

@@ -84,6 +84,8 @@ hipError_t launch_wsgemm(const GemmParams& p, hipStream_t stream);
 // 256-byte header, then the hand-off of wsgemm_split_partial_bytes(M, N).
 hipError_t launch_wsgemm_ws(const GemmParams& p, void* workspace, int compute_units,
                             hipStream_t stream);
+// Whether launch_wsgemm_ws splits K for this shape (beyond 64 tokens it must).
+bool wsgemm_ws_splits(int M, int N, int K, int compute_units);
 hipError_t launch_attnres(const AttnParams& p, hipStream_t stream);
 hipError_t launch_fused(const FusedParams& p, hipStream_t stream);
 hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t stream);

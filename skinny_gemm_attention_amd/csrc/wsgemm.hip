@@ -57,6 +57,8 @@ __global__ __launch_bounds__(512) void wsgemm_kernel(GemmParams p, int R) {
 // partial equals the sentinel) and finish; part S-1 polls them, adds the parts
 // in part order (its own last), re-arms the words, rounds and writes y 16
 // bytes at a time. Only the last part waits, and only on lower workgroup ids.
+// Up to 128 tokens (eight 16-token tiles) stream through one pass: W is read
+// once for all of them (the pages' token groups serve the same end).
 // S (2 or 4) is a run-time argument: hipcc emitted the host launch stub of
 // only one of two kernel instantiations that differed in nothing but S.
 constexpr int kMaxSplit = 4;
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(512) void wsgemm_split_kernel(GemmParams p, unsigne
                                                            int S) {
   using C = GemmLdsSplit<TT>;
   static_assert(C::NT == 512, "launch bounds");
-  static_assert(C::NP * C::kQuads * 16 + 64 * kSplitRows * 2 <= C::kLdsBytes, "y tile fits");
+  static_assert(C::NP * C::kQuads * 16 + TT * 16 * kSplitRows * 2 <= C::kLdsBytes, "y tile fits");
   constexpr int QPT = (C::kQuads + C::NT - 1) / C::NT;
   __shared__ __attribute__((aligned(16))) char lds[C::kLdsBytes];
   f32x4* red = reinterpret_cast<f32x4*>(lds);  // reused once the ring is drained
@@ -178,10 +180,12 @@ __global__ __launch_bounds__(512) void wsgemm_split_kernel(GemmParams p, unsigne
     }
   }
   lds_barrier();
-  const int om = tid >> 3, oj = tid & 7;
-  if (om < p.M && 8 * oj < rows)
-    st16(p.y + (size_t)om * p.ldy + row0 + 8 * oj,
-         *reinterpret_cast<const u32x4*>(tile + om * (kSplitRows / 2) + 4 * oj));
+  for (int it = tid; it < p.M * 8; it += C::NT) {  // 16 bytes (8 rows) of one token each
+    const int om = it >> 3, oj = it & 7;
+    if (8 * oj < rows)
+      st16(p.y + (size_t)om * p.ldy + row0 + 8 * oj,
+           *reinterpret_cast<const u32x4*>(tile + om * (kSplitRows / 2) + 4 * oj));
+  }
 }
 
 template <int RT, int TT>
@@ -220,17 +224,28 @@ static hipError_t go_split(const GemmParams& p, unsigned* partials, FusedWorkspa
   return hipGetLastError();
 }
 
+bool wsgemm_ws_splits(int M, int N, int K, int compute_units) {
+  const int ng = (N + kSplitRows - 1) / kSplitRows;
+  return M > 32 && 2 * ng <= compute_units && K >= 256;
+}
+
 hipError_t launch_wsgemm_ws(const GemmParams& p, void* workspace, int compute_units,
                             hipStream_t stream) {
   const int tt = (p.M + 15) / 16;
   const int ng = (p.N + kSplitRows - 1) / kSplitRows;
   const int S = kMaxSplit * ng <= compute_units ? kMaxSplit : 2 * ng <= compute_units ? 2 : 1;
-  if (tt < 3 || S == 1 || p.K < 256) return launch_wsgemm(p, stream);
+  if (!wsgemm_ws_splits(p.M, p.N, p.K, compute_units)) return launch_wsgemm(p, stream);
   FusedWorkspace* ws = static_cast<FusedWorkspace*>(workspace);
   unsigned* partials =
       reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + kWorkspaceHeader);
-  return tt == 3 ? go_split<3>(p, partials, ws, ng, S, stream)
-                 : go_split<4>(p, partials, ws, ng, S, stream);
+  switch (tt) {
+    case 3: return go_split<3>(p, partials, ws, ng, S, stream);
+    case 4: return go_split<4>(p, partials, ws, ng, S, stream);
+    case 5: return go_split<5>(p, partials, ws, ng, S, stream);
+    case 6: return go_split<6>(p, partials, ws, ng, S, stream);
+    case 7: return go_split<7>(p, partials, ws, ng, S, stream);
+    default: return go_split<8>(p, partials, ws, ng, S, stream);
+  }
 }
 
 }  // namespace attnres

@@ -224,6 +224,7 @@ def test_wsgemm_workspace_size(lib):
     assert lib.wsgemm_workspace_size(32, 4096) == 256
     assert lib.wsgemm_workspace_size(64, 4096) == 256 + 3 * 64 * 1024 * 16
     assert lib.wsgemm_workspace_size(33, 1000) == 256 + 3 * 16 * 768 * 16
+    assert lib.wsgemm_workspace_size(128, 4096) == 256 + 3 * 64 * 2048 * 16
     assert lib.wsgemm_workspace_size(-1, 8) == 0
 
 
@@ -236,8 +237,10 @@ def call_gemm_ws(lib, ws=A, wsb=256 + 3 * 64 * 1024 * 16, **kw):
 
 @pytest.mark.parametrize("change,code", [
     (dict(ws=None), -5), (dict(ws=A + 16), -5), (dict(wsb=256), -5),
-    (dict(x=None), -1), (dict(M=65), -3), (dict(N=4100), -4), (dict(ldy=4088), -1),
+    (dict(x=None), -1), (dict(M=129), -3), (dict(N=4100), -4), (dict(ldy=4088), -1),
     (dict(x=A + 8), -2),
+    # beyond 64 tokens only the K split serves: K >= 256 and 2 ceil(N/64) <= 256
+    (dict(M=65, K=248, ldx=248, ldw=248), -4), (dict(M=65, N=16392, ldy=16392), -4),
 ])
 def test_wsgemm_run_ws_rejects(lib, change, code):
     assert call_gemm_ws(lib, **change) == code

@@ -148,3 +148,21 @@ def test_wsgemm_ws_reuses_its_workspace_and_is_deterministic():
     c = run_gemm_ws(x2, W2, ws)  # fewer tokens, same workspace
     assert np.array_equal(a, b)
     assert_bf16_close(c, oracle.gemm(x2, W2, nthreads=16), "reused workspace")
+
+
+@pytest.mark.parametrize("M", [65, 96, 128])
+def test_wsgemm_ws_beyond_64_tokens(M):
+    """One pass over W for up to 128 tokens (K split four ways at N = 4096)."""
+    x, W = synth.gemm_inputs(M, 4096, 7168, seed=M)
+    y = run_gemm_ws(x, W)
+    assert_bf16_close(y, oracle.gemm(x, W, nthreads=16), f"wsgemm_ws M={M}")
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 4096, 7168), (100, 1000, 1000), (128, 8, 264),
+                                   (80, 7168, 520), (113, 264, 8200)])
+def test_wsgemm_ws_beyond_64_tokens_exact_integers(M, N, K):
+    xi = rng.integers(-8, 9, (M, K))
+    wi = rng.integers(-8, 9, (N, K))
+    x, W = bits_of(xi), bits_of(wi)
+    y = run_gemm_ws(x, W, ldy=N + 8)
+    assert np.array_equal(y, oracle.gemm(x, W, nthreads=16))
