@@ -171,7 +171,9 @@ int wsgemm_run_ws(const void* x, int64_t ldx, const void* W, int64_t ldw, void* 
 /*
  * attnres_oproj_workspace_size - bytes of device workspace attnres_oproj_run
  * needs for M tokens and hidden width H (nb does not change it): a 256-byte
- * header and one bf16 mailbox row per token.
+ * header, one bf16 mailbox row per token and, beyond 32 tokens, one FP32 row
+ * per token (token count rounded up to a multiple of 16): the partial products
+ * that one of the two workgroups splitting K hands to the other.
  */
 size_t attnres_oproj_workspace_size(int M, int H, int nb);
 
