@@ -183,7 +183,8 @@ size_t attnres_oproj_workspace_size(int M, int H, int nb);
  * Every attnres_oproj_run call leaves the workspace armed again. The first
  * 32-bit word of the header becomes nonzero if a call ever gave up waiting
  * for its own workgroups (a safety bound of about a second per wait that a
- * healthy device never reaches); that call's outputs are then invalid.
+ * healthy device never reaches); that call's outputs are then invalid, and
+ * the workspace must be prepared again by this call before its next use.
  *   workspace: device memory, 256-byte aligned; bytes: a multiple of 4, at
  *   least 256.
  */
