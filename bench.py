@@ -117,6 +117,32 @@ def graph_time_us(torch, step, steps, warmup):
     return e0.elapsed_time(e1) * 1e3 / steps
 
 
+def stream_read_gbs(torch, sga, dev, gb, reps=10):
+    """Streaming-read bandwidth: attnres_stream_read over a `gb` GB buffer,
+    `reps` launches between HIP events on one stream (one warm-up launch)."""
+    n = int(gb * 1e9) // 16 * 16
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    sink = torch.empty(sga.STREAM_READ_SINK_WORDS, dtype=torch.int32, device=dev)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        sga.attnres_stream_read(src, sink, stream)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            sga.attnres_stream_read(src, sink, stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del src, sink
+    torch.cuda.empty_cache()
+    return {"gbs": round(n / (us * 1e-6) / 1e9, 1), "bytes": n, "us_per_pass": round(us, 2),
+            "kernel": "stream_read_kernel (attnres_stream_read): 16-byte non-temporal loads, "
+                      "65536 workgroups x 512 threads, grid-stride",
+            "frac_of_peak": round(n / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def side_configs(args, np, torch, sga, synth):
     """Standalone AttnRes (T=256, nb = 0..8, final boundary), standalone GEMM
     (K=7168, N=4096, M = 1, 8, 16, 64) or the look-ahead statistics: one JSON
@@ -308,6 +334,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bounded host time for the oracle baseline (0 skips it)")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--stream-read-gb", type=float, default=2.0,
+                    help="size of the streaming-read reference measurement (0: skip)")
     ap.add_argument("--calibrate-copy-mb", type=float, default=0.0,
                     help="also run 3 plain device copies of this many MB (for scaling "
                          "HBM byte counters read under a profiler); 0 skips them")
@@ -455,6 +483,13 @@ def main():
                             "null unless measured on these kernel sources",
         },
     }
+
+    if args.stream_read_gb > 0:
+        # what a plain 16-byte non-temporal read of HBM reaches on this device
+        # (attnres_stream_read), beside the 8 TB/s spec figure
+        rd = stream_read_gbs(torch, sga, dev, args.stream_read_gb)
+        result["stream_read"] = rd
+        result["pct_of_measured_read_bw"] = round(100.0 * gbs / rd["gbs"], 1)
 
     if args.cpu_seconds > 0:
         import oracle

@@ -270,6 +270,25 @@ int attnres_post_run(const void* delta, int64_t ld_delta, void* prefix, int64_t 
 /* attnres_strerror - a static, human-readable description of a return code. */
 const char* attnres_strerror(int code);
 
+/*
+ * attnres_stream_read - a measurement helper, not a step of the method: it
+ * reads `bytes` bytes at src exactly once with 16-byte non-temporal loads
+ * spread over the whole device, the access pattern of a plain HBM stream,
+ * so that the streaming-read bandwidth this device reaches can be set beside
+ * the roofline figures of the kernels above. Each of its
+ * ATTNRES_STREAM_READ_SINK_WORDS workgroups stores the XOR of the 32-bit words
+ * it read to sink[workgroup] (so no load can be dropped); the XOR of all sink
+ * words is the XOR of every word of src.
+ *   src: device memory, 16-byte aligned, NULL only when bytes == 0;
+ *   bytes: a multiple of 16.
+ *   sink: device memory for ATTNRES_STREAM_READ_SINK_WORDS 32-bit words,
+ *   4-byte aligned; every word is written.
+ * Errors: ATTNRES_EINVAL (NULL sink or src), ATTNRES_EALIGN (src or bytes not
+ * a multiple of 16, sink not 4-byte aligned), ATTNRES_EHIP.
+ */
+#define ATTNRES_STREAM_READ_SINK_WORDS 65536
+int attnres_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,6 +48,8 @@ _lib.attnres_oproj_ahead_run.argtypes = [_P, _I64, _P, _I64, _I, _P, _I64, _P, _
                                          _I, _I, _P, _P, _F, _P, _I64, _P, _P, _SZ, _P]
 _lib.attnres_post_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I, _P, _P, _P, _P, _I64,
                                   _P, _I64, _P, _I64, _P, _F, _F, _I, _I, _I, _I, _I, _I, _P]
+_lib.attnres_stream_read.argtypes = [_P, _SZ, _P, _P]
+_lib.attnres_stream_read.restype = _I
 _lib.attnres_strerror.argtypes = [_I]
 _lib.attnres_strerror.restype = ctypes.c_char_p
 for _f in (_lib.attnres_run, _lib.wsgemm_run, _lib.wsgemm_run_ws, _lib.wsgemm_moe_front_run,
@@ -59,7 +61,9 @@ EXPORTS = ("attnres_run", "wsgemm_run", "wsgemm_moe_front_run", "wsgemm_workspac
            "wsgemm_run_ws",
            "attnres_oproj_run", "attnres_oproj_workspace_size",
            "attnres_oproj_workspace_init", "attnres_oproj_ahead_run", "attnres_post_run",
-           "attnres_strerror")
+           "attnres_strerror", "attnres_stream_read")
+
+STREAM_READ_SINK_WORDS = 65536  # ATTNRES_STREAM_READ_SINK_WORDS
 
 
 class AttnResError(RuntimeError):
@@ -111,6 +115,21 @@ def _stream(stream):
 def _check(rc: int, where: str):
     if rc != 0:
         raise AttnResError(rc, where)
+
+
+def attnres_stream_read(src, sink, stream=None):
+    """Measurement helper: reads every byte of the contiguous device tensor src
+    once (16-byte non-temporal loads); sink (STREAM_READ_SINK_WORDS 32-bit
+    words) receives one XOR of the words each workgroup read."""
+    if not src.is_contiguous():
+        raise AttnResError(-1, "attnres_stream_read: src must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() * sink.element_size() < 4 * STREAM_READ_SINK_WORDS:
+        raise AttnResError(-1, "attnres_stream_read: sink too small")
+    rc = _lib.attnres_stream_read(ctypes.c_void_p(src.data_ptr() if nbytes else 0), nbytes,
+                                  ctypes.c_void_p(sink.data_ptr()), _stream(stream))
+    _check(rc, "attnres_stream_read")
+    return sink
 
 
 def wsgemm_run(x, W, y, stream=None):

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattnres.so")
-SOURCES = ["api.hip", "wsgemm.hip", "attnres.hip", "fused.hip"]
+SOURCES = ["api.hip", "wsgemm.hip", "attnres.hip", "fused.hip", "stream_read.hip"]
 HEADERS = ["common.hpp", "token.hpp", "gemm.hpp", "launch.hpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -5,6 +5,13 @@
 #include "../../include/attnres.h"
 #include "launch.hpp"
 
+namespace attnres {
+// stream_read.hip: reads `bytes` (a multiple of 16) at src once; workgroup
+// g < grid stores the XOR of the words it read to sink[g].
+hipError_t launch_stream_read(const void* src, size_t bytes, unsigned* sink, int grid,
+                              hipStream_t stream);
+}  // namespace attnres
+
 namespace {
 
 using attnres::AttnParams;
@@ -346,6 +353,16 @@ int attnres_post_run(const void* delta, int64_t ld_delta, void* prefix, int64_t 
     p.sscal = scal;
   }
   return from_hip(attnres::launch_attnres(p, static_cast<hipStream_t>(stream)));
+}
+
+int attnres_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!sink || (!src && bytes > 0)) return ATTNRES_EINVAL;
+  if ((bytes & 15u) != 0 || (src && !aligned16(src)) ||
+      (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+    return ATTNRES_EALIGN;
+  return from_hip(attnres::launch_stream_read(src, bytes, static_cast<unsigned*>(sink),
+                                              ATTNRES_STREAM_READ_SINK_WORDS,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 const char* attnres_strerror(int code) {

@@ -38,6 +38,8 @@ def lib():
                                           P, SZ, P]
     L.attnres_post_run.argtypes = [P, I64, P, I64, P, I64, I64, I, P, P, P, P, I64, P, I64, P, I64,
                                    P, F, F, I, I, I, I, I, I, P]
+    L.attnres_stream_read.argtypes = [P, SZ, P, P]
+    L.attnres_stream_read.restype = I
     L.attnres_strerror.argtypes = [I]
     L.attnres_strerror.restype = ctypes.c_char_p
     return L
@@ -54,7 +56,8 @@ def test_header_symbols_exported(lib):
                           "wsgemm_moe_front_run",
                           "attnres_oproj_workspace_size",
                           "attnres_oproj_workspace_init", "attnres_oproj_run",
-                          "attnres_oproj_ahead_run", "attnres_post_run", "attnres_strerror"}
+                          "attnres_oproj_ahead_run", "attnres_post_run", "attnres_strerror",
+                          "attnres_stream_read"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -272,3 +275,21 @@ def test_wsgemm_moe_front_run_rejects(lib, change, code):
 
 def test_wsgemm_moe_front_run_empty_is_a_noop(lib):
     assert call_moe(lib, M=0) == 0
+
+
+def test_stream_read_host_checks(lib):
+    """attnres_stream_read rejects bad arguments on the host (nothing is
+    launched: the pointers below are never dereferenced)."""
+    fake = ctypes.c_void_p(1 << 40)  # 16-byte aligned, never touched
+    assert lib.attnres_stream_read(fake, 64, None, None) == -1          # no sink
+    assert lib.attnres_stream_read(None, 64, fake, None) == -1          # no source
+    assert lib.attnres_stream_read(fake, 40, fake, None) == -2          # bytes % 16
+    assert lib.attnres_stream_read(ctypes.c_void_p((1 << 40) + 8), 64, fake, None) == -2
+    assert lib.attnres_stream_read(fake, 64, ctypes.c_void_p((1 << 40) + 2), None) == -2
+
+
+def test_stream_read_sink_words_match_header():
+    import skinny_gemm_attention_amd as sga
+
+    m = re.search(r"#define ATTNRES_STREAM_READ_SINK_WORDS (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == sga.STREAM_READ_SINK_WORDS
