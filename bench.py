@@ -52,6 +52,8 @@ FOOTPRINT = 640e6
 KERNEL_SOURCES = ("common.hpp", "token.hpp", "gemm.hpp", "launch.hpp", "fused.hip")
 MEASURED_TRAFFIC = {
     1: {"digest": "b2a283858466250a9835da360b30c9c018ee0774990dcad3ec3c318e45f978bf", "fetch": 60976115, "write": 1103025},
+    0: {"digest": "b2a283858466250a9835da360b30c9c018ee0774990dcad3ec3c318e45f978bf", "fetch": 14953449, "write": 137627},
+    2: {"digest": "b2a283858466250a9835da360b30c9c018ee0774990dcad3ec3c318e45f978bf", "fetch": 139280283, "write": 10092544},
 }
 
 WORKLOADS = {
