@@ -107,6 +107,40 @@ def _row_stride(t):
     return t.stride(-2) if t.dim() >= 2 else t.shape[-1]
 
 
+def _rows(t, rows, cols, name):
+    """t is a 2-D tensor with at least rows x cols elements (the kernels index
+    it by those counts: a smaller tensor would be read or written out of
+    bounds)."""
+    if t is None:
+        return
+    if t.dim() != 2 or t.shape[0] < rows or t.shape[1] < cols:
+        raise AttnResError(-1, f"{name} must be [>= {rows}, >= {cols}], got {tuple(t.shape)}")
+
+
+def _vec(t, n, name):
+    if t is None:
+        return
+    if t.dim() != 1 or t.shape[0] < n:
+        raise AttnResError(-1, f"{name} must hold >= {n} elements, got {tuple(t.shape)}")
+
+
+def _blocks(t, T, H):
+    """blocks [>= T, cap, >= H] (the library checks nb and write against cap)."""
+    if t is None:
+        return
+    if t.dim() != 3 or t.shape[0] < T or t.shape[2] < H:
+        raise AttnResError(-1, f"blocks must be [>= {T}, cap, >= {H}], got {tuple(t.shape)}")
+
+
+def _attn_shapes(T, H, prefix, blocks, norm, query, out_norm, out, aux):
+    _rows(prefix, T, H, "prefix")
+    _rows(out, T, H, "out")
+    _rows(aux, T, H, "aux")
+    _blocks(blocks, T, H)
+    for t, name in ((norm, "norm"), (query, "query"), (out_norm, "out_norm")):
+        _vec(t, H, name)
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -136,6 +170,8 @@ def wsgemm_run(x, W, y, stream=None):
     """y[M, N] = bf16(x[M, K] W[N, K]^T) (-0.0 stored as +0.0)."""
     M, K = x.shape
     N = W.shape[0]
+    _rows(W, N, K, "W")
+    _rows(y, M, N, "y")
     rc = _lib.wsgemm_run(_ptr(x), _row_stride(x), _ptr(W), _row_stride(W), _ptr(y),
                          _row_stride(y), M, N, K, _stream(stream))
     _check(rc, "wsgemm_run")
@@ -148,6 +184,8 @@ def wsgemm_moe_front_run(x, W, out, *, router_base, slot, base, valid, split, st
     c >= split as bf16 at column base + c - split, the rows between dropped."""
     M, K = x.shape
     N = W.shape[0]
+    _rows(W, N, K, "W")
+    _rows(out, M, 0, "out")  # the library checks the columns against the row stride
     rc = _lib.wsgemm_moe_front_run(_ptr(x), _row_stride(x), _ptr(W), _row_stride(W), _ptr(out),
                                    _row_stride(out), M, N, K, router_base, slot, base, valid,
                                    split, _stream(stream))
@@ -169,6 +207,8 @@ def wsgemm_run_ws(x, W, y, workspace, stream=None):
     """wsgemm_run with a workspace (K split across workgroups beyond 32 tokens)."""
     M, K = x.shape
     N = W.shape[0]
+    _rows(W, N, K, "W")
+    _rows(y, M, N, "y")
     rc = _lib.wsgemm_run_ws(_ptr(x), _row_stride(x), _ptr(W), _row_stride(W), _ptr(y),
                             _row_stride(y), M, N, K, ctypes.c_void_p(workspace.data_ptr()),
                             workspace.numel() * workspace.element_size(), _stream(stream))
@@ -180,6 +220,7 @@ def attnres_run(delta, prefix, blocks, norm, query, out_norm, out, aux=None, *, 
                 has_delta=1, final_boundary=0, eps=1e-6, out_eps=1e-6, stream=None):
     """AttnRes of T = delta.shape[0] tokens; blocks [T, cap, H] (any token / slot strides)."""
     T, H = delta.shape
+    _attn_shapes(T, H, prefix, blocks, norm, query, out_norm, out, aux)
     if blocks is None:
         bst_t = bst_b = cap = 0
     else:
@@ -220,6 +261,8 @@ def attnres_oproj_run(x, W, prefix, blocks, norm, query, out_norm, out, aux, wor
     """Fused o-projection + AttnRes: delta = bf16(x W^T), then AttnRes (T = M)."""
     M, K = x.shape
     H = W.shape[0]
+    _rows(W, H, K, "W")
+    _attn_shapes(M, H, prefix, blocks, norm, query, out_norm, out, aux)
     if blocks is None:
         bst_t = bst_b = cap = 0
     else:
@@ -254,6 +297,13 @@ def attnres_oproj_ahead_run(x, W, prefix, blocks, norm, query, out_norm, out, au
     saved blocks: mixture [M, H] and scal [M, 2] (maximum, exp_sum), float32."""
     M, K = x.shape
     H = W.shape[0]
+    _rows(W, H, K, "W")
+    _attn_shapes(M, H, prefix, blocks, norm, query, out_norm, out, aux)
+    _vec(next_norm, H, "next_norm")
+    _vec(next_query, H, "next_query")
+    _rows(mixture, M, H, "mixture")
+    if scal is not None and scal.numel() < 2 * M:
+        raise AttnResError(-1, f"scal must hold >= {2 * M} floats")
     bst_t, bst_b, cap = _block_strides(blocks)
     ws = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -276,6 +326,10 @@ def attnres_post_run(delta, prefix, blocks, norm, query, out_norm, out, aux, mix
     """AttnRes post() on carried saved-block statistics (mixture [T, H] and scal
     [T, 2], float32, of nb saved blocks); blocks is only written (slot write)."""
     T, H = delta.shape
+    _attn_shapes(T, H, prefix, blocks, norm, query, out_norm, out, aux)
+    _rows(mixture, T, H, "mixture")
+    if scal is not None and scal.numel() < 2 * T:
+        raise AttnResError(-1, f"scal must hold >= {2 * T} floats")
     bst_t, bst_b, cap = _block_strides(blocks)
     if mixture is not None and mixture.stride(-1) != 1:
         raise AttnResError(-1, "mixture rows must be contiguous")
