@@ -22,31 +22,53 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
   __shared__ float lds_pre[wg_sum_lds<16, NW>], lds_post[wg_sum_lds<4, NW>],
       lds_fin[wg_sum_lds<1, NW>];
   const int t = blockIdx.x, tid = threadIdx.x, CH = a.H >> 3;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-
-  u32x4 vb[kMaxBlocks][NCH], g[NCH], d[NCH], p[NCH], sm[NCH][2];
-  float w[NCH][8];
+  // Every load of the token is a raw buffer load issued before any result is
+  // used: a saved block past nb, an unused tensor (num_records 0) or a lane
+  // past the row (an offset past the end) reads zeros without touching
+  // memory. (Loads written as `cond ? ld16(p) : 0` became branches whose
+  // register copies made the compiler wait for every earlier load in the
+  // middle of the sequence.)
+  const int H2 = a.H * 2;
+  auto rsrc = [](const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferDword3);
+  };
+  const __amdgpu_buffer_rsrc_t r_norm = rsrc(a.norm, H2), r_query = rsrc(a.query, H2),
+                               r_gain = rsrc(a.out_norm, H2),
+                               r_delta = rsrc(a.delta + (size_t)t * a.ld_delta, H2),
+                               r_prefix = rsrc(a.prefix + (size_t)t * a.ld_prefix,
+                                               a.has_delta ? H2 : 0),
+                               r_smix = rsrc(STATS ? a.smix + (size_t)t * a.ld_smix : nullptr,
+                                             (STATS && a.nb > 0) ? 2 * H2 : 0);
+  u32x4 vb[kMaxBlocks][NCH], g[NCH], d[NCH], p[NCH], sm[NCH][2], nq[NCH][2];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = tid + j * NT;
     const bool valid = c < CH;
-    const size_t col = (size_t)c * 8;
+    const unsigned off = valid ? (unsigned)c * 16u : kBufferOff;       // bf16 rows
+    const unsigned off4 = valid ? (unsigned)c * 32u : kBufferOff;      // FP32 rows
+    nq[j][0] = __builtin_amdgcn_raw_buffer_load_b128(r_norm, off, 0, 0);
+    nq[j][1] = __builtin_amdgcn_raw_buffer_load_b128(r_query, off, 0, 0);
 #pragma unroll
-    for (int b = 0; b < kMaxBlocks; ++b)
-      vb[b][j] = (!STATS && valid && b < a.nb) ? ld16(a.blocks + t * a.bst_t + b * a.bst_b + col)
-                                               : zero;
-    const bool sv = STATS && valid && a.nb > 0;
-    sm[j][0] = sv ? ld16(a.smix + t * a.ld_smix + col) : zero;
-    sm[j][1] = sv ? ld16(a.smix + t * a.ld_smix + col + 4) : zero;
-    g[j] = valid ? ld16(a.out_norm + col) : zero;
-    d[j] = valid ? ld16(a.delta + t * a.ld_delta + col) : zero;
-    p[j] = (valid && a.has_delta) ? ld16(a.prefix + t * a.ld_prefix + col) : zero;
-    if (valid) {
-      weights8(a, c, w[j]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[j][i] = 0.0f;
+    for (int b = 0; b < kMaxBlocks; ++b) {
+      const bool live = !STATS && b < a.nb;  // blocks may be NULL when nb == 0
+      const __amdgpu_buffer_rsrc_t r_blk =
+          rsrc(live ? a.blocks + (size_t)t * a.bst_t + (size_t)b * a.bst_b : a.blocks, live ? H2 : 0);
+      vb[b][j] = __builtin_amdgcn_raw_buffer_load_b128(r_blk, off, 0, 0);
     }
+    sm[j][0] = __builtin_amdgcn_raw_buffer_load_b128(r_smix, off4, 0, 0);
+    sm[j][1] = __builtin_amdgcn_raw_buffer_load_b128(r_smix, valid ? off4 + 16u : kBufferOff, 0, 0);
+    g[j] = __builtin_amdgcn_raw_buffer_load_b128(r_gain, off, 0, 0);
+    d[j] = __builtin_amdgcn_raw_buffer_load_b128(r_delta, off, 0, 0);
+    p[j] = __builtin_amdgcn_raw_buffer_load_b128(r_prefix, off, 0, 0);
+  }
+  float w[NCH][8];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    float n[8], q[8];
+    unpack8(nq[j][0], n);
+    unpack8(nq[j][1], q);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[j][i] = n[i] * q[i];  // exact: product of two bf16
   }
 
   // pre: saved-block statistics and the unnormalised mixture
