@@ -27,7 +27,11 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
   // past the row (an offset past the end) reads zeros without touching
   // memory. (Loads written as `cond ? ld16(p) : 0` became branches whose
   // register copies made the compiler wait for every earlier load in the
-  // middle of the sequence.)
+  // middle of the sequence.) The token's saved blocks, delta and old prefix
+  // are read once: non-temporal (measured at T = 256: 13.5 -> 11.4 us at
+  // nb = 8, 5.76 -> 5.38 us at nb = 0). The gains, read by every workgroup,
+  // and the carried mixture keep the default policy (a non-temporal mixture
+  // read made attnres_post_run slower, 6.13 -> 6.58 us).
   const int H2 = a.H * 2;
   auto rsrc = [](const void* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferDword3);
@@ -53,13 +57,13 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
       const bool live = !STATS && b < a.nb;  // blocks may be NULL when nb == 0
       const __amdgpu_buffer_rsrc_t r_blk =
           rsrc(live ? a.blocks + (size_t)t * a.bst_t + (size_t)b * a.bst_b : a.blocks, live ? H2 : 0);
-      vb[b][j] = __builtin_amdgcn_raw_buffer_load_b128(r_blk, off, 0, 0);
+      vb[b][j] = __builtin_amdgcn_raw_buffer_load_b128(r_blk, off, 0, kCacheNTLoad);
     }
     sm[j][0] = __builtin_amdgcn_raw_buffer_load_b128(r_smix, off4, 0, 0);
     sm[j][1] = __builtin_amdgcn_raw_buffer_load_b128(r_smix, valid ? off4 + 16u : kBufferOff, 0, 0);
     g[j] = __builtin_amdgcn_raw_buffer_load_b128(r_gain, off, 0, 0);
-    d[j] = __builtin_amdgcn_raw_buffer_load_b128(r_delta, off, 0, 0);
-    p[j] = __builtin_amdgcn_raw_buffer_load_b128(r_prefix, off, 0, 0);
+    d[j] = __builtin_amdgcn_raw_buffer_load_b128(r_delta, off, 0, kCacheNTLoad);
+    p[j] = __builtin_amdgcn_raw_buffer_load_b128(r_prefix, off, 0, kCacheNTLoad);
   }
   float w[NCH][8];
 #pragma unroll

@@ -46,9 +46,7 @@ inline size_t split_partial_bytes(int M, int H) {
 // kSpinLimit rounds (about a second); a workgroup that gives up flags the
 // workspace and finishes.
 constexpr int kSpinLimit = 1 << 20;
-constexpr unsigned kBufferOff = 0xFFFFFFF0u;  // past num_records: reads zeros
-constexpr int kBufferDword3 = 0x00020000;     // raw buffer, 32-bit data format
-constexpr int kCacheSC1 = 16;                 // buffer-load cache policy: device scope
+constexpr int kCacheSC1 = 16;  // buffer-load cache policy: device scope
 
 // Hand-off bytes of wsgemm_run_ws for M tokens and N rows: up to three parts
 // per 64-row group (four-way split), one 16-byte quad per MFMA output quad.
