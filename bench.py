@@ -51,9 +51,9 @@ FOOTPRINT = 640e6
 # sources differ.
 KERNEL_SOURCES = ("common.hpp", "token.hpp", "gemm.hpp", "launch.hpp", "fused.hip")
 MEASURED_TRAFFIC = {
-    1: {"digest": "b2a283858466250a9835da360b30c9c018ee0774990dcad3ec3c318e45f978bf", "fetch": 60976115, "write": 1103025},
-    0: {"digest": "b2a283858466250a9835da360b30c9c018ee0774990dcad3ec3c318e45f978bf", "fetch": 14953449, "write": 137627},
-    2: {"digest": "b2a283858466250a9835da360b30c9c018ee0774990dcad3ec3c318e45f978bf", "fetch": 139280283, "write": 10092544},
+    1: {"digest": "0a90522dec1459a8db29a859b01bf84fc60822459abb86aadfb458003dc98c5a", "fetch": 60994582, "write": 1100991},
+    0: {"digest": "0a90522dec1459a8db29a859b01bf84fc60822459abb86aadfb458003dc98c5a", "fetch": 14932546, "write": 137477},
+    2: {"digest": "0a90522dec1459a8db29a859b01bf84fc60822459abb86aadfb458003dc98c5a", "fetch": 139188264, "write": 10092544},
 }
 
 WORKLOADS = {
