@@ -51,9 +51,9 @@ FOOTPRINT = 640e6
 # sources differ.
 KERNEL_SOURCES = ("common.hpp", "token.hpp", "gemm.hpp", "launch.hpp", "fused.hip")
 MEASURED_TRAFFIC = {
-    1: {"digest": "0a90522dec1459a8db29a859b01bf84fc60822459abb86aadfb458003dc98c5a", "fetch": 60994582, "write": 1100991},
-    0: {"digest": "0a90522dec1459a8db29a859b01bf84fc60822459abb86aadfb458003dc98c5a", "fetch": 14932546, "write": 137477},
-    2: {"digest": "0a90522dec1459a8db29a859b01bf84fc60822459abb86aadfb458003dc98c5a", "fetch": 139188264, "write": 10092544},
+    1: {"digest": "545d0194a4dbad4150c4f171853aaeb5cf4761402c1f8ba417013a1a2e9cc9ce", "fetch": 61012209, "write": 988721},
+    0: {"digest": "545d0194a4dbad4150c4f171853aaeb5cf4761402c1f8ba417013a1a2e9cc9ce", "fetch": 14932110, "write": 123252},
+    2: {"digest": "545d0194a4dbad4150c4f171853aaeb5cf4761402c1f8ba417013a1a2e9cc9ce", "fetch": 139186737, "write": 9175040},
 }
 
 WORKLOADS = {

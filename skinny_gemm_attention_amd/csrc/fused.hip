@@ -414,16 +414,16 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
   }
   absorb(todo);
   // re-arm the collected mailbox words for the next call (device scope, like
-  // every mailbox access); nothing below waits for these stores
+  // every mailbox access), one 16-byte store per chunk (two 8-byte stores
+  // were 0.18 us slower per step at 8 tokens); nothing below waits for them
 #pragma unroll
   for (int k = 0; k < KT; ++k)
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int c = tid + j * NT;
       if (k < ntok && c < CH) {
-        unsigned* wbox = f.mailbox + (size_t)tok[k] * (a.H >> 1) + (size_t)c * 4;
-        st8_device(wbox, u32x2{kMailboxSentinel, kMailboxSentinel});
-        st8_device(wbox + 2, u32x2{kMailboxSentinel, kMailboxSentinel});
+        const u32x4 sent = {kMailboxSentinel, kMailboxSentinel, kMailboxSentinel, kMailboxSentinel};
+        __builtin_amdgcn_raw_buffer_store_b128(sent, mbox, (unsigned)tok[k] * (unsigned)(2 * a.H) + 16u * (unsigned)c, 0, kCacheSC1);
       }
     }
   float pp[4 * KT];
