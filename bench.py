@@ -51,9 +51,9 @@ FOOTPRINT = 640e6
 # sources differ.
 KERNEL_SOURCES = ("common.hpp", "token.hpp", "gemm.hpp", "launch.hpp", "fused.hip")
 MEASURED_TRAFFIC = {
-    1: {"digest": "545d0194a4dbad4150c4f171853aaeb5cf4761402c1f8ba417013a1a2e9cc9ce", "fetch": 61012209, "write": 988721},
-    0: {"digest": "545d0194a4dbad4150c4f171853aaeb5cf4761402c1f8ba417013a1a2e9cc9ce", "fetch": 14932110, "write": 123252},
-    2: {"digest": "545d0194a4dbad4150c4f171853aaeb5cf4761402c1f8ba417013a1a2e9cc9ce", "fetch": 139186737, "write": 9175040},
+    1: {"digest": "52f20028aaaaa59d7654aed5e5ee430f61de853959bc2f2cdfd000537263c92f", "fetch": 60991285, "write": 988548},
+    0: {"digest": "52f20028aaaaa59d7654aed5e5ee430f61de853959bc2f2cdfd000537263c92f", "fetch": 14933920, "write": 123381},
+    2: {"digest": "52f20028aaaaa59d7654aed5e5ee430f61de853959bc2f2cdfd000537263c92f", "fetch": 139173039, "write": 9175040},
 }
 
 WORKLOADS = {

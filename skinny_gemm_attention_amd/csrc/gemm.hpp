@@ -253,12 +253,13 @@ struct GemmLds {
 };
 
 // Chunk shape per tile shape (measured on MI355X): 512-byte row segments in
-// four slots for two row tiles and one token tile; 1 KiB segments in three
-// slots for a single row tile; 512-byte segments beyond 16 tokens, where x
-// dominates a chunk.
+// four slots for two row tiles and one token tile; 1 KiB segments in four
+// slots (128 KB) for a single row tile (wsgemm_run at M <= 16, N = 4096: 5%
+// faster than three slots; five do not fit beside the fused kernel's other
+// LDS); 512-byte segments beyond 16 tokens, where x dominates a chunk.
 template <int RT, int TT>
 using GemmLdsFor = GemmLds<RT, TT, (TT == 1 && RT == 1 ? 1024 : 512),
-                           (TT == 1 ? (RT == 1 ? 3 : 4) : TT == 2 ? 4 : 3)>;
+                           (TT == 1 ? 4 : TT == 2 ? 4 : 3)>;
 
 // Split-K tiles for more than 32 tokens: 64 rows (four row tiles) per
 // workgroup over half of K, 256-byte row segments in four slots; wavefronts
