@@ -44,26 +44,35 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
                                r_smix = rsrc(STATS ? a.smix + (size_t)t * a.ld_smix : nullptr,
                                              (STATS && a.nb > 0) ? 2 * H2 : 0);
   u32x4 vb[kMaxBlocks][NCH], g[NCH], d[NCH], p[NCH], sm[NCH][2], nq[NCH][2];
+  unsigned off[NCH], off4[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = tid + j * NT;
     const bool valid = c < CH;
-    const unsigned off = valid ? (unsigned)c * 16u : kBufferOff;       // bf16 rows
-    const unsigned off4 = valid ? (unsigned)c * 32u : kBufferOff;      // FP32 rows
-    nq[j][0] = __builtin_amdgcn_raw_buffer_load_b128(r_norm, off, 0, 0);
-    nq[j][1] = __builtin_amdgcn_raw_buffer_load_b128(r_query, off, 0, 0);
+    off[j] = valid ? (unsigned)c * 16u : kBufferOff;    // bf16 rows
+    off4[j] = valid ? (unsigned)c * 32u : kBufferOff;   // FP32 rows
+    nq[j][0] = __builtin_amdgcn_raw_buffer_load_b128(r_norm, off[j], 0, 0);
+    nq[j][1] = __builtin_amdgcn_raw_buffer_load_b128(r_query, off[j], 0, 0);
+  }
+  // what pre needs first: every saved block of both chunks, then the rest
+  // (loads complete in issue order, so pre then waits for no delta, prefix or
+  // gain: 1-5% faster at T = 256 for nb >= 2)
+#pragma unroll
+  for (int j = 0; j < NCH; ++j)
 #pragma unroll
     for (int b = 0; b < kMaxBlocks; ++b) {
       const bool live = !STATS && b < a.nb;  // blocks may be NULL when nb == 0
       const __amdgpu_buffer_rsrc_t r_blk =
           rsrc(live ? a.blocks + (size_t)t * a.bst_t + (size_t)b * a.bst_b : a.blocks, live ? H2 : 0);
-      vb[b][j] = __builtin_amdgcn_raw_buffer_load_b128(r_blk, off, 0, kCacheNTLoad);
+      vb[b][j] = __builtin_amdgcn_raw_buffer_load_b128(r_blk, off[j], 0, kCacheNTLoad);
     }
-    sm[j][0] = __builtin_amdgcn_raw_buffer_load_b128(r_smix, off4, 0, 0);
-    sm[j][1] = __builtin_amdgcn_raw_buffer_load_b128(r_smix, valid ? off4 + 16u : kBufferOff, 0, 0);
-    g[j] = __builtin_amdgcn_raw_buffer_load_b128(r_gain, off, 0, 0);
-    d[j] = __builtin_amdgcn_raw_buffer_load_b128(r_delta, off, 0, kCacheNTLoad);
-    p[j] = __builtin_amdgcn_raw_buffer_load_b128(r_prefix, off, 0, kCacheNTLoad);
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    sm[j][0] = __builtin_amdgcn_raw_buffer_load_b128(r_smix, off4[j], 0, 0);
+    sm[j][1] = __builtin_amdgcn_raw_buffer_load_b128(r_smix, off4[j] == kBufferOff ? kBufferOff : off4[j] + 16u, 0, 0);
+    g[j] = __builtin_amdgcn_raw_buffer_load_b128(r_gain, off[j], 0, 0);
+    d[j] = __builtin_amdgcn_raw_buffer_load_b128(r_delta, off[j], 0, kCacheNTLoad);
+    p[j] = __builtin_amdgcn_raw_buffer_load_b128(r_prefix, off[j], 0, kCacheNTLoad);
   }
   float w[NCH][8];
 #pragma unroll
