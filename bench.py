@@ -51,9 +51,9 @@ FOOTPRINT = 640e6
 # sources differ.
 KERNEL_SOURCES = ("common.hpp", "token.hpp", "gemm.hpp", "launch.hpp", "fused.hip")
 MEASURED_TRAFFIC = {
-    1: {"digest": "52f20028aaaaa59d7654aed5e5ee430f61de853959bc2f2cdfd000537263c92f", "fetch": 60991285, "write": 988548},
-    0: {"digest": "52f20028aaaaa59d7654aed5e5ee430f61de853959bc2f2cdfd000537263c92f", "fetch": 14933920, "write": 123381},
-    2: {"digest": "52f20028aaaaa59d7654aed5e5ee430f61de853959bc2f2cdfd000537263c92f", "fetch": 139173039, "write": 9175040},
+    1: {"digest": "531aafd4eec435f5cd94eb0b8557dc07d5d3a7fb06a70d512318039e2d75af71", "fetch": 60981881, "write": 991400},
+    0: {"digest": "531aafd4eec435f5cd94eb0b8557dc07d5d3a7fb06a70d512318039e2d75af71", "fetch": 14932957, "write": 123390},
+    2: {"digest": "531aafd4eec435f5cd94eb0b8557dc07d5d3a7fb06a70d512318039e2d75af71", "fetch": 139224343, "write": 9175040},
 }
 
 WORKLOADS = {
