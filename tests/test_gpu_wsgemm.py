@@ -54,7 +54,11 @@ def test_wsgemm_config4(M):
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 7168), (8, 7168, 1024), (13, 1000, 1000),
                                    (16, 4096, 7168), (33, 264, 520), (64, 7168, 4096),
                                    (64, 8, 8), (5, 16384, 64), (17, 96, 1016), (49, 520, 24),
-                                   (2, 7168, 1032), (31, 40, 8200)])
+                                   (2, 7168, 1032), (31, 40, 8200),
+                                   # the 16-row tile (N <= 4096, M <= 16), four-slot ring of
+                                   # 512-element chunks: K below one chunk, a ragged third
+                                   # chunk, more chunks than slots with a ragged tail
+                                   (3, 40, 8), (9, 4096, 1048), (16, 256, 4104), (1, 4096, 2568)])
 def test_wsgemm_exact_integers(M, N, K):
     xi = rng.integers(-8, 9, (M, K))
     wi = rng.integers(-8, 9, (N, K))
