@@ -56,6 +56,8 @@ def _load():
         lib.oracle_moe_front.restype = ctypes.c_int
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_round_bf16.restype = ctypes.c_uint16
+        lib.oracle_round_bf16_n.argtypes = [P, P, I64]
+        lib.oracle_round_bf16_n.restype = None
         for f in ("oracle_gemm", "oracle_attnres", "oracle_attnres_streaming",
                   "oracle_attnres_oproj", "oracle_attnres_pre", "oracle_attnres_post"):
             getattr(lib, f).restype = ctypes.c_int
@@ -73,6 +75,14 @@ def _u16(a):
 
 def round_bf16(z: float) -> int:
     return int(_load().oracle_round_bf16(float(z)))
+
+
+def round_bf16_array(z) -> np.ndarray:
+    """``round_bf16`` of every element of the float64 array ``z`` (same shape)."""
+    z = np.ascontiguousarray(z, dtype=np.float64)
+    out = np.zeros(z.shape, np.uint16)
+    _load().oracle_round_bf16_n(_p(z), _p(out), z.size)
+    return out
 
 
 def gemm(x, W, nthreads: int = 1, exact: bool = False):

@@ -123,17 +123,20 @@ typedef struct {
   int N, K;
 } gemm_ctx;
 
-static void gemm_rows(void* p, int lo, int hi) {
+/* Output elements [lo, hi) in row-major (m, n) order: each one is the same
+ * ascending-k sum whichever thread computes it, so the split over threads
+ * (by element, so that a single token still spreads over every thread) does
+ * not change any result. */
+static void gemm_elems(void* p, int lo, int hi) {
   gemm_ctx* c = (gemm_ctx*)p;
-  for (int m = lo; m < hi; ++m) {
-    for (int n = 0; n < c->N; ++n) {
-      double s = 0.0;
-      for (int k = 0; k < c->K; ++k) s += bf(c->x[m * c->ldx + k]) * bf(c->W[n * c->ldw + k]);
-      if (c->yexact) c->yexact[(int64_t)m * c->N + n] = s;
-      uint16_t r = rn_bf16(s);
-      if (r == 0x8000) r = 0; /* -0.0 is stored as +0.0 (positive_zero) */
-      c->y[m * c->ldy + n] = r;
-    }
+  for (int i = lo; i < hi; ++i) {
+    const int m = i / c->N, n = i % c->N;
+    double s = 0.0;
+    for (int k = 0; k < c->K; ++k) s += bf(c->x[m * c->ldx + k]) * bf(c->W[n * c->ldw + k]);
+    if (c->yexact) c->yexact[(int64_t)m * c->N + n] = s;
+    uint16_t r = rn_bf16(s);
+    if (r == 0x8000) r = 0; /* -0.0 is stored as +0.0 (positive_zero) */
+    c->y[m * c->ldy + n] = r;
   }
 }
 
@@ -142,8 +145,9 @@ static void gemm_rows(void* p, int lo, int hi) {
 int oracle_gemm(const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* y,
                 int64_t ldy, double* yexact, int M, int N, int K, int nthreads) {
   if (!x || !W || !y || M < 0 || N < 0 || K < 0 || ldx < K || ldw < K || ldy < N) return OR_EINVAL;
+  if ((int64_t)M * N > 0x7FFFFFFF) return OR_EINVAL;
   gemm_ctx c = {x, W, ldx, ldw, ldy, y, yexact, N, K};
-  parallel_ranges(gemm_rows, &c, M, nthreads);
+  parallel_ranges(gemm_elems, &c, M * N, nthreads);
   return OR_OK;
 }
 
@@ -649,3 +653,9 @@ int oracle_moe_front(const uint16_t* x, int64_t ldx, const uint16_t* W, int64_t 
 
 /* Exposed for the pins of the rounding rule. */
 uint16_t oracle_round_bf16(double z) { return rn_bf16(z); }
+
+/* The same rounding over n values (the parity tests build the bounds of a
+ * bfloat16 sum from it). */
+void oracle_round_bf16_n(const double* z, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = rn_bf16(z[i]);
+}

@@ -79,6 +79,18 @@ def test_round_matches_torch_conversion():
     assert np.array_equal(ours[~double_round], theirs[~double_round])
 
 
+def test_round_array_equals_scalar_rounding():
+    """The array form is the scalar rule applied per element (golden cases,
+    zeros of both signs, subnormals and random magnitudes)."""
+    vals = [0.0, -0.0, 2.0 ** -133, -(2.0 ** -134), 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8,
+            -(1.0 + 2.0 ** -8), 3.0e38, 2.0 ** -126 * 1.5]
+    x = np.concatenate([np.array(vals), rng.standard_normal(4991) * np.exp2(
+        rng.integers(-140, 120, 4991))]).reshape(50, -1)
+    got = oracle.round_bf16_array(x)
+    want = np.array([oracle.round_bf16(v) for v in x.ravel()], np.uint16).reshape(x.shape)
+    assert got.shape == x.shape and np.array_equal(got, want)
+
+
 # --------------------------------------------------------------------------
 # GEMM pins (O-1 .. O-4)
 # --------------------------------------------------------------------------
@@ -138,6 +150,12 @@ def test_gemm_matches_numpy_matmul():
 def test_gemm_threads_bit_identical():
     x, W = synth.gemm_inputs(9, 64, 256, seed=2)
     assert np.array_equal(oracle.gemm(x, W, nthreads=1), oracle.gemm(x, W, nthreads=4))
+    # one token: the element split still spreads it over every thread, with the
+    # same bits and the same exact sums
+    x1 = x[:1]
+    a, ea = oracle.gemm(x1, W, nthreads=1, exact=True)
+    b, eb = oracle.gemm(x1, W, nthreads=7, exact=True)
+    assert np.array_equal(a, b) and np.array_equal(ea, eb)
 
 
 # --------------------------------------------------------------------------
