@@ -51,6 +51,7 @@ extern "C" {
 #define ATTNRES_EUNSUPPORTED (-4) /* shape the kernels do not cover (H, N, K limits below) */
 #define ATTNRES_EWORKSPACE (-5)   /* workspace missing, too small or misaligned */
 #define ATTNRES_EHIP (-6)         /* the HIP runtime refused the launch */
+#define ATTNRES_EWAIT (-7)        /* a wait of an earlier call on the workspace gave up */
 
 /* Limits. */
 #define ATTNRES_MAX_BLOCKS 8 /* saved blocks scored per token (nb) */
@@ -160,9 +161,10 @@ size_t wsgemm_workspace_size(int M, int N);
  * ATTNRES_EUNSUPPORTED.
  *   workspace: at least wsgemm_workspace_size(M, N) bytes, 256-byte aligned,
  *   prepared once by attnres_oproj_workspace_init (the same format); every
- *   call leaves it prepared again, and its first 32-bit word nonzero if a
- *   wait gave up (the safety bound of attnres_oproj_run). Calls that may run
- *   at the same time need distinct workspaces.
+ *   call leaves it prepared again. If a wait gave up (the safety bound of
+ *   attnres_oproj_run) the workspace stays flagged as described there
+ *   (attnres_workspace_status). Calls that may run at the same time need
+ *   distinct workspaces.
  * Errors: those of wsgemm_run, and ATTNRES_EWORKSPACE.
  */
 int wsgemm_run_ws(const void* x, int64_t ldx, const void* W, int64_t ldw, void* y, int64_t ldy,
@@ -183,12 +185,27 @@ size_t attnres_oproj_workspace_size(int M, int H, int nb);
  * Every attnres_oproj_run call leaves the workspace armed again. The first
  * 32-bit word of the header becomes nonzero if a call ever gave up waiting
  * for its own workgroups (a safety bound of about a second per wait that a
- * healthy device never reaches); that call's outputs are then invalid, and
- * the workspace must be prepared again by this call before its next use.
+ * healthy device never reaches). That call's outputs are then invalid, and
+ * every later call on the flagged workspace is accepted but writes nothing
+ * at all, until this call prepares the workspace again;
+ * attnres_workspace_status reports the flag.
  *   workspace: device memory, 256-byte aligned; bytes: a multiple of 4, at
  *   least 256.
  */
 int attnres_oproj_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attnres_workspace_status - whether a wait of a call on this workspace
+ * (attnres_oproj_run, attnres_oproj_ahead_run, wsgemm_run_ws) gave up: waits
+ * until the work enqueued on `stream` so far has finished (it synchronises
+ * the host with the stream; not for use under stream capture), then reads the
+ * workspace header.
+ * Returns ATTNRES_OK (no wait gave up: the outputs of every call so far are
+ * valid), ATTNRES_EWAIT (a wait gave up: see attnres_oproj_workspace_init),
+ * ATTNRES_EWORKSPACE (NULL, fewer than 256 bytes or not 256-byte aligned) or
+ * ATTNRES_EHIP (the copy or the synchronisation failed).
+ */
+int attnres_workspace_status(const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attnres_oproj_run - the fused decode step: the o-projection of x (the

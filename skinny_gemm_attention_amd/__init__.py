@@ -48,6 +48,8 @@ _lib.attnres_oproj_ahead_run.argtypes = [_P, _I64, _P, _I64, _I, _P, _I64, _P, _
                                          _I, _I, _P, _P, _F, _P, _I64, _P, _P, _SZ, _P]
 _lib.attnres_post_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I, _P, _P, _P, _P, _I64,
                                   _P, _I64, _P, _I64, _P, _F, _F, _I, _I, _I, _I, _I, _I, _P]
+_lib.attnres_workspace_status.argtypes = [_P, _SZ, _P]
+_lib.attnres_workspace_status.restype = _I
 _lib.attnres_stream_read.argtypes = [_P, _SZ, _P, _P]
 _lib.attnres_stream_read.restype = _I
 _lib.attnres_strerror.argtypes = [_I]
@@ -61,9 +63,10 @@ EXPORTS = ("attnres_run", "wsgemm_run", "wsgemm_moe_front_run", "wsgemm_workspac
            "wsgemm_run_ws",
            "attnres_oproj_run", "attnres_oproj_workspace_size",
            "attnres_oproj_workspace_init", "attnres_oproj_ahead_run", "attnres_post_run",
-           "attnres_strerror", "attnres_stream_read")
+           "attnres_strerror", "attnres_stream_read", "attnres_workspace_status")
 
 STREAM_READ_SINK_WORDS = 65536  # ATTNRES_STREAM_READ_SINK_WORDS
+EWAIT = -7  # ATTNRES_EWAIT: a wait of an earlier call on the workspace gave up
 
 
 class AttnResError(RuntimeError):
@@ -185,7 +188,14 @@ def wsgemm_moe_front_run(x, W, out, *, router_base, slot, base, valid, split, st
     M, K = x.shape
     N = W.shape[0]
     _rows(W, N, K, "W")
-    _rows(out, M, 0, "out")  # the library checks the columns against the row stride
+    # the library bounds the columns by the row stride; a column-sliced view
+    # is narrower than its stride, so its own width is checked here
+    width = 0
+    if valid > 0:
+        width = router_base + 2 * (slot + valid)
+    if split < N:
+        width = max(width, base + N - split)
+    _rows(out, M, width, "out")
     rc = _lib.wsgemm_moe_front_run(_ptr(x), _row_stride(x), _ptr(W), _row_stride(W), _ptr(out),
                                    _row_stride(out), M, N, K, router_base, slot, base, valid,
                                    split, _stream(stream))
@@ -240,6 +250,27 @@ def attnres_oproj_workspace_size(M: int, H: int, nb: int) -> int:
     return int(_lib.attnres_oproj_workspace_size(M, H, nb))
 
 
+def attnres_workspace_status(workspace, stream=None) -> int:
+    """Waits for the work enqueued on the stream, then returns 0 when no wait of
+    a call on this workspace gave up, EWAIT when one did (that call's outputs
+    are invalid and later calls write nothing until the workspace is re-armed
+    by attnres_oproj_workspace_init)."""
+    rc = _lib.attnres_workspace_status(ctypes.c_void_p(workspace.data_ptr()),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream))
+    if rc not in (0, EWAIT):
+        raise AttnResError(rc, "attnres_workspace_status")
+    return rc
+
+
+workspace_status = attnres_workspace_status
+
+
+def check_workspace(workspace, stream=None):
+    """Raises AttnResError(EWAIT) if a wait of a call on this workspace gave up."""
+    _check(attnres_workspace_status(workspace, stream), "attnres_workspace_status")
+
+
 def attnres_oproj_workspace_init(workspace, stream=None):
     """Arms a workspace once after allocation (see attnres_oproj_workspace_init)."""
     rc = _lib.attnres_oproj_workspace_init(ctypes.c_void_p(workspace.data_ptr()),
@@ -258,7 +289,11 @@ def make_workspace(M: int, H: int, nb: int, device="cuda") -> torch.Tensor:
 def attnres_oproj_run(x, W, prefix, blocks, norm, query, out_norm, out, aux, workspace, *, nb,
                       write=-1, has_delta=1, final_boundary=0, eps=1e-6, out_eps=1e-6,
                       stream=None):
-    """Fused o-projection + AttnRes: delta = bf16(x W^T), then AttnRes (T = M)."""
+    """Fused o-projection + AttnRes: delta = bf16(x W^T), then AttnRes (T = M).
+
+    The call only enqueues work. Its outputs are valid when
+    attnres_workspace_status(workspace) returns 0 afterwards (a wait that gave
+    up, a safety bound a healthy device never reaches, leaves them invalid)."""
     M, K = x.shape
     H = W.shape[0]
     _rows(W, H, K, "W")

@@ -355,6 +355,18 @@ int attnres_post_run(const void* delta, int64_t ld_delta, void* prefix, int64_t 
   return from_hip(attnres::launch_attnres(p, static_cast<hipStream_t>(stream)));
 }
 
+int attnres_workspace_status(const void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes < attnres::kWorkspaceHeader ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return ATTNRES_EWORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned word = 0;
+  if (hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return ATTNRES_EHIP;
+  return word == 0 ? ATTNRES_OK : ATTNRES_EWAIT;
+}
+
 int attnres_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
   if (!sink || (!src && bytes > 0)) return ATTNRES_EINVAL;
   if ((bytes & 15u) != 0 || (src && !aligned16(src)) ||
@@ -374,6 +386,9 @@ const char* attnres_strerror(int code) {
     case ATTNRES_EUNSUPPORTED: return "shape not supported (H, N or K limits)";
     case ATTNRES_EWORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case ATTNRES_EHIP: return "HIP launch failed";
+    case ATTNRES_EWAIT:
+      return "a wait in an earlier call on this workspace gave up: that call's results are invalid "
+             "and later calls write nothing until attnres_oproj_workspace_init re-arms it";
     default: return "unknown error code";
   }
 }

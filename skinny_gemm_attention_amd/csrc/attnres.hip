@@ -86,11 +86,11 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
 
   // pre: saved-block statistics and the unnormalised mixture
   float mix[NCH][8];
-  PreScalars pre = {0.0f, 0.0f};
+  BlockStats pre = {0.0f, 0.0f};
   if (STATS) {
     if (a.nb > 0) {
-      pre.maxl = a.sscal[2 * t];
-      pre.S = a.sscal[2 * t + 1];
+      pre.anchor = a.sscal[2 * t];
+      pre.total = a.sscal[2 * t + 1];
     }
 #pragma unroll
     for (int j = 0; j < NCH; ++j)
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
     float ps[16];
     pre_partials(vb, w, a.nb, ps);
     wg_sum<16, NW>(ps, lds_pre);
-    pre = pre_finish(ps, vb, a.nb, a.eps, a.inv_h, mix);
+    pre = block_stats(ps, vb, a.nb, a.eps, a.inv_h, mix);
   } else {
 #pragma unroll
     for (int j = 0; j < NCH; ++j)
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
       mg[j][i] = mix[j][i] * gg[j][i];
     }
   }
-  finish_out<NT, NCH>(a, t, out_scalars(a, pre, pp), nw, ng, mix, mg, gg, lds_fin);
+  finish_out<NT, NCH>(a, t, out_coefs(a, pre, pp), nw, ng, mix, mg, gg, lds_fin);
 }
 
 hipError_t launch_attnres(const AttnParams& p, hipStream_t stream) {

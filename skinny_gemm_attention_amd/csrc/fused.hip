@@ -33,8 +33,18 @@
 // (sc1) store; each owner thread polls its own 8-column chunks with
 // device-scope loads, in a fixed chunk order, and re-arms them after reading.
 // One memory latency separates a store from its consumer; no counter, fence or
-// cache write-back is involved. A spin limit bounds every wait: an owner that
-// gives up records it in the workspace header and finishes.
+// cache write-back is involved. A spin limit bounds every wait: a workgroup
+// that gives up records it in the workspace header and carries on to the end
+// (every thread still reaches every barrier; that call's outputs are
+// invalid). A call whose workspace header is already set writes nothing, so
+// a flagged workspace stays unusable until it is re-armed: in a GEMM
+// workgroup thread 0 reads the header as it starts and shares it at the
+// barrier after the W stream, and the workgroup returns before its first
+// store; in an owner each wavefront reads it as it starts, skips its
+// look-ahead stores and returns before polling. (A wavefront that has ended
+// no longer takes part in its workgroup's barriers. Returning before pre(),
+// right after the first loads, made the compiler wait for every outstanding
+// load before each LDS read of the W stream: 64 tokens, K = 8192, 30.7 -> 42.7 us.)
 #include "gemm.hpp"
 #include "launch.hpp"
 
@@ -87,6 +97,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
   f32x4* red = reinterpret_cast<f32x4*>(sm.ring);
   __shared__ float lds_pre[wg_sum_lds<(4 * KT > 16 ? 4 * KT : 16), NW>],
       lds_fin[wg_sum_lds<1, NW>];
+  __shared__ unsigned lds_flag;  // GEMM role: thread 0's reading of the workspace flag
 
   const AttnParams& a = f.a;
   const int g = blockIdx.x, tid = threadIdx.x, CH = a.H >> 3;
@@ -101,6 +112,10 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
     // contiguous halves; alternating 256 B to 2 KB pieces was 6-10% slower.)
     // The first workgroup never waits; the second waits only on a lower
     // workgroup id.
+    // nonzero: an earlier call on this workspace gave up a wait, so this call
+    // writes nothing (read by thread 0, shared at the barrier after the ring)
+    const unsigned flag0 =
+        tid == 0 ? __hip_atomic_load(&f.ws->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
     const bool second = SPLIT && g >= f.ng;
     const int rg = SPLIT ? (second ? g - f.ng : g) : g;
     const int row0 = rg * R;
@@ -142,7 +157,9 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
       core.finish();
       core.stash(red);
     }
+    if (tid == 0) lds_flag = flag0;
     lds_barrier();
+    if (lds_flag) return;  // the whole workgroup: the same LDS word after the barrier
     f32x4 s[QPT];
 #pragma unroll
     for (int i = 0; i < QPT; ++i) s[i] = qv[i] ? C::gather(red, tid + i * NT) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -189,7 +206,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
           }
         }
         if (pending == 0) break;
-        if (spin >= kSpinLimit) {
+        if (spin >= kSpinLimit) {  // gave up: flag the workspace (results invalid)
           __hip_atomic_store(&f.ws->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
           for (int i = 0; i < QPT; ++i)
@@ -232,7 +249,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
       }
       // re-arm the first workgroup's partials after the stores the owners wait
       // for (before them, the mailbox posts queued behind 16 KB of re-arm
-      // stores: config 2 0.09 us slower)
+      // stores: 0.09 us slower at 64 tokens, K = 8192)
       const u32x4 sent = {kMailboxSentinel, kMailboxSentinel, kMailboxSentinel, kMailboxSentinel};
 #pragma unroll
       for (int i = 0; i < QPT; ++i)
@@ -273,17 +290,23 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
   for (int k = 0; k < KT; ++k)
     if (o + k * NO < M) ntok = k + 1;
 
+  // nonzero: an earlier call on this workspace gave up a wait, so this call
+  // writes nothing. Each wavefront reads it and returns as a whole before its
+  // first store; a wavefront that has ended no longer takes part in the
+  // workgroup's barriers, so the others never wait for it.
+  const unsigned flagw = __builtin_amdgcn_readfirstlane(
+      __hip_atomic_load(&f.ws->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   float gg[NCH][8], w[NCH][8], w2[AHEAD ? NCH : 1][8];
   token_weights<NT, NCH>(a, w, gg);
   if constexpr (AHEAD) pair_weights<NT, NCH>(f.ah.norm, f.ah.query, a.H, w2);
-  PreScalars pre[KT];
+  BlockStats pre[KT];
   // one token: its mixture (and mixture*gains) stay in registers; more
   // tokens park their mixtures in LDS
   float mix1[kOne ? NCH : 1][8], mg1[kOne ? NCH : 1][8];
   float pm2[KT][NCH];  // per-chunk sums of mix^2 (the post partial that needs no new prefix)
 #pragma unroll
   for (int k = 0; k < KT; ++k) {
-    pre[k] = PreScalars{0.0f, 0.0f};
+    pre[k] = BlockStats{0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < NCH; ++j) pm2[k][j] = 0.0f;
     if (k < ntok) {
@@ -295,18 +318,19 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
         // non-temporal stores: a later kernel reads them (normal stores cost
         // about 2 us at 64 tokens)
         float mix2[NCH][8];
-        PreScalars pre2;
+        BlockStats pre2;
         token_pre2<NT, NCH>(a, t, w, w2, f.ah.eps, mix, mix2, pre[k], pre2, lds_pre);
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
           const int c = tid + j * NT;
-          if (c < CH) {
+          if (c < CH && !flagw) {
             float* dst = f.ah.mix + (size_t)t * f.ah.ld_mix + (size_t)c * 8;
             __builtin_nontemporal_store(f32x4{mix2[j][0], mix2[j][1], mix2[j][2], mix2[j][3]}, reinterpret_cast<f32x4*>(dst));
             __builtin_nontemporal_store(f32x4{mix2[j][4], mix2[j][5], mix2[j][6], mix2[j][7]}, reinterpret_cast<f32x4*>(dst + 4));
           }
         }
-        if (tid == 0) st8(f.ah.scal + 2 * (size_t)t, __builtin_bit_cast(u32x2, f32x2{pre2.maxl, pre2.S}));
+        if (tid == 0 && !flagw)
+          st8(f.ah.scal + 2 * (size_t)t, __builtin_bit_cast(u32x2, f32x2{pre2.anchor, pre2.total}));
       } else {
         pre[k] = token_pre<NT, NCH>(a, t, w, mix, lds_pre);
       }
@@ -335,6 +359,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
   // arrives (its mix^2 partial already in pre); once the last chunk is in,
   // the mailbox words are re-armed and only the reduction and the output
   // remain.
+  if (flagw) return;  // nothing stored yet (the look-ahead stores above skip it too)
   int tok[KT];
 #pragma unroll
   for (int k = 0; k < KT; ++k) tok[k] = k < ntok ? o + k * NO : o;
@@ -412,7 +437,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
         }
       }
     if (pending == 0) break;
-    if (spin >= kSpinLimit) {
+    if (spin >= kSpinLimit) {  // gave up: flag the workspace (results invalid)
       __hip_atomic_store(&f.ws->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
@@ -477,7 +502,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
         }
       }
       const float tot[4] = {pp[4 * k], pp[4 * k + 1], pp[4 * k + 2], pp[4 * k + 3]};
-      finish_out<NT, NCH>(a, t, out_scalars(a, pre[k], tot), nw, ng, mix, mg, gg, lds_fin);
+      finish_out<NT, NCH>(a, t, out_coefs(a, pre[k], tot), nw, ng, mix, mg, gg, lds_fin);
       if (a.final_b) lds_barrier();  // lds_fin is reused by the next token
     }
   }

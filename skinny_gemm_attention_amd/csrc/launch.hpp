@@ -58,7 +58,9 @@ inline size_t wsgemm_split_partial_bytes(int M, int N) {
 }
 
 struct FusedWorkspace {
-  unsigned error;  // nonzero after an owner gave up waiting (results invalid)
+  // nonzero after a wait gave up (that call's results are invalid); every
+  // later call on the workspace then writes nothing until it is re-armed
+  unsigned error;
 };
 
 struct FusedParams {

@@ -56,7 +56,9 @@ __global__ __launch_bounds__(512) void wsgemm_kernel(GemmParams p, int R) {
 // sentinel-armed hand-off of the fused call; stored zeros are +0.0, so no
 // partial equals the sentinel) and finish; part S-1 polls them, adds the parts
 // in part order (its own last), re-arms the words, rounds and writes y 16
-// bytes at a time. Only the last part waits, and only on lower workgroup ids.
+// bytes at a time. Only the last part waits, and only on lower workgroup ids;
+// a part that gives up flags the workspace header (its results are invalid),
+// and a call on a flagged workspace writes nothing at all.
 // Up to 128 tokens (eight 16-token tiles) stream through one pass: W is read
 // once for all of them (the pages' token groups serve the same end).
 // S (2 or 4) is a run-time argument: hipcc emitted the host launch stub of
@@ -78,6 +80,11 @@ __global__ __launch_bounds__(512) void wsgemm_split_kernel(GemmParams p, unsigne
   const int rows = min(kSplitRows, p.N - row0);
   const int kbeg = q * kpart;
   const int klen = max(0, min(kpart, p.K - kbeg));
+  // nonzero: an earlier call on this workspace gave up a wait, so this call
+  // writes nothing (read by thread 0, used by the workgroup after a barrier)
+  __shared__ unsigned lds_flag;
+  const unsigned flag0 =
+      tid == 0 ? __hip_atomic_load(&ws->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
   int qm[QPT], qr[QPT];
   bool qv[QPT];
 #pragma unroll
@@ -96,7 +103,9 @@ __global__ __launch_bounds__(512) void wsgemm_split_kernel(GemmParams p, unsigne
     core.finish();
     core.stash(red);
   }
+  if (tid == 0) lds_flag = flag0;
   lds_barrier();
+  if (lds_flag) return;  // the whole workgroup: the same LDS word after the barrier
   f32x4 s[QPT];
 #pragma unroll
   for (int i = 0; i < QPT; ++i) s[i] = qv[i] ? C::gather(red, tid + i * C::NT) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -152,7 +161,7 @@ __global__ __launch_bounds__(512) void wsgemm_split_kernel(GemmParams p, unsigne
         }
       }
     if (pending == 0) break;
-    if (spin >= kSpinLimit) {
+    if (spin >= kSpinLimit) {  // gave up: flag the workspace (results invalid)
       __hip_atomic_store(&ws->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }

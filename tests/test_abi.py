@@ -38,6 +38,8 @@ def lib():
                                           P, SZ, P]
     L.attnres_post_run.argtypes = [P, I64, P, I64, P, I64, I64, I, P, P, P, P, I64, P, I64, P, I64,
                                    P, F, F, I, I, I, I, I, I, P]
+    L.attnres_workspace_status.argtypes = [P, SZ, P]
+    L.attnres_workspace_status.restype = I
     L.attnres_stream_read.argtypes = [P, SZ, P, P]
     L.attnres_stream_read.restype = I
     L.attnres_strerror.argtypes = [I]
@@ -57,7 +59,7 @@ def test_header_symbols_exported(lib):
                           "attnres_oproj_workspace_size",
                           "attnres_oproj_workspace_init", "attnres_oproj_run",
                           "attnres_oproj_ahead_run", "attnres_post_run", "attnres_strerror",
-                          "attnres_stream_read"}
+                          "attnres_stream_read", "attnres_workspace_status"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -71,7 +73,7 @@ def test_binding_names_match_header():
 
 def test_strerror_and_workspace(lib):
     codes = {0: b"success", -1: b"invalid", -2: b"aligned", -3: b"range", -4: b"supported",
-             -5: b"workspace", -6: b"HIP"}
+             -5: b"workspace", -6: b"HIP", -7: b"gave up"}
     for c, word in codes.items():
         assert word in lib.attnres_strerror(c)
     assert b"unknown" in lib.attnres_strerror(-99)
@@ -293,3 +295,20 @@ def test_stream_read_sink_words_match_header():
 
     m = re.search(r"#define ATTNRES_STREAM_READ_SINK_WORDS (\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == sga.STREAM_READ_SINK_WORDS
+
+
+def test_workspace_status_host_checks(lib):
+    """attnres_workspace_status rejects a missing, short or misaligned
+    workspace before any HIP call (the pointers are never dereferenced)."""
+    fake = 1 << 40
+    assert lib.attnres_workspace_status(None, 4096, None) == -5
+    assert lib.attnres_workspace_status(ctypes.c_void_p(fake), 255, None) == -5
+    assert lib.attnres_workspace_status(ctypes.c_void_p(fake + 16), 4096, None) == -5
+
+
+def test_error_codes_match_header():
+    import skinny_gemm_attention_amd as sga
+
+    text = open(HEADER).read()
+    codes = dict((n, int(v)) for n, v in re.findall(r"#define ATTNRES_(E\w+) \((-\d+)\)", text))
+    assert codes["EWAIT"] == sga.EWAIT == -7

@@ -88,3 +88,17 @@ def test_well_shaped_cpu_tensors_reach_the_device_check():
     with pytest.raises(sga.AttnResError, match="GPU"):
         sga.attnres_oproj_run(t(M, K), t(H, K), a["prefix"], a["blocks"], a["norm"], a["query"],
                               a["out_norm"], a["out"], a["aux"], t(1024, dtype=torch.uint8), nb=NB)
+
+
+@pytest.mark.parametrize("kw,width", [
+    (dict(router_base=64, slot=2, base=0, valid=40, split=48), 64 + 2 * (2 + 40)),  # router end
+    (dict(router_base=0, slot=0, base=200, valid=0, split=64), 200 + H - 64),       # latent end
+])
+def test_moe_front_out_width(kw, width):
+    """The MoE-front destination must be as wide as the columns the epilogue
+    writes (a column-sliced view is narrower than its row stride)."""
+    wide = t(M, 1024)
+    with pytest.raises(sga.AttnResError, match="out"):
+        sga.wsgemm_moe_front_run(t(M, K), t(H, K), wide[:, :width - 2], **kw)
+    with pytest.raises(sga.AttnResError, match="GPU"):  # wide enough: reaches the device check
+        sga.wsgemm_moe_front_run(t(M, K), t(H, K), wide[:, :width], **kw)
