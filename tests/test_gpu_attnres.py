@@ -156,3 +156,49 @@ def test_attnres_many_tokens(T, H, nb, cap, write, has_delta, final, aux, pad,
     else:
         check(s, r, nb=nb, write=write, has_delta=has_delta, final=final, aux=aux,
               what=f"T={T} H={H} nb={nb}")
+
+
+def _special_pairs(T, H, *, negative_zero_delta, seed):
+    """prefix / delta bit patterns mixing ordinary values with signed zeros,
+    bfloat16 subnormals, the smallest normals and exact cancellations."""
+    rng = np.random.default_rng(seed)
+    tiny = [0x0000, 0x8000, 0x0001, 0x8001, 0x0003, 0x8003, 0x0040, 0x807F, 0x0080, 0x8080,
+            0x3FC0, 0xBFC0]  # +-0, subnormals, smallest normals, +-1.5
+    s = synth.decode_step(T, None, 1, H=H, cap=2, seed=seed)
+    prefix, delta = s.prefix.copy(), s.delta.copy()
+    special = rng.random((T, H)) < 0.6
+    prefix[special] = rng.choice(tiny, size=int(special.sum()))
+    delta[special] = rng.choice(tiny, size=int(special.sum()))
+    cancel = special & (rng.random((T, H)) < 0.4)
+    delta[cancel] = prefix[cancel] ^ 0x8000  # x + (-x): an exact zero
+    if not negative_zero_delta:  # the fused call's delta: -0.0 is stored as +0.0
+        delta[delta == 0x8000] = 0x0000
+    s.prefix, s.delta = prefix, delta
+    return s
+
+
+@pytest.mark.parametrize("has_delta", [1, 0])
+def test_residual_add_keeps_signed_zeros_and_subnormals(has_delta):
+    """The new prefix bf16(prefix + delta) with signed zeros, subnormals and
+    exact cancellations is the oracle's bit for bit, and with a delta that
+    never holds -0.0 (the projection's, -0.0 made +0.0 as on the gemm.ws_gemm
+    page, positive_zero) it never holds -0.0 either: an exact zero sum is
+    +0.0 and subnormals are neither flushed nor sign-flipped. The fused call's
+    mailbox relies on this, since its sentinel is the pair (+0.0, -0.0)."""
+    s = _special_pairs(4, 1024, negative_zero_delta=False, seed=11)
+    r = run(s, nb=1, write=1, has_delta=has_delta, final=0)
+    ref = check(s, r, nb=1, write=1, has_delta=has_delta, final=0, what="signed zeros")
+    assert not np.any(r["prefix"] == 0x8000), "a new prefix element is -0.0"
+    assert np.count_nonzero((r["prefix"] & 0x7F80) == 0) > 1000  # zeros and subnormals present
+    if has_delta:
+        assert np.any((r["prefix"] & 0x7FFF) != 0) and np.array_equal(r["prefix"], ref.prefix)
+
+
+def test_residual_add_negative_zero_delta_matches_oracle():
+    """With -0.0 in the delta (which the fused call never passes), -0.0 + -0.0
+    is -0.0 on both sides: the sum is the IEEE one, bit for bit."""
+    s = _special_pairs(4, 1024, negative_zero_delta=True, seed=12)
+    r = run(s, nb=1, write=-1, has_delta=1, final=1)
+    ref = check(s, r, nb=1, write=-1, has_delta=1, final=1, what="negative-zero delta")
+    both = (s.prefix == 0x8000) & (s.delta == 0x8000)
+    assert both.any() and np.all(ref.prefix[both] == 0x8000)
