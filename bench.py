@@ -1,29 +1,35 @@
 """Benchmark of the fused o-projection + AttnRes decode step on one MI355X.
 
-Default workload: M = 8 tokens, K = 4096, N = H = 7168, nb = 4 saved blocks,
+Headline workload: M = 8 tokens, K = 4096, N = H = 7168, nb = 4 saved blocks,
 non-write layer (delta path), one aux copy, non-final boundary. One "step" is
 one attnres_oproj_run call (one launch of the fused kernel) over one batch.
+The same run also times the other two workloads the metric names (M = 1,
+K = 1024, nb = 1; M = 64, K = 8192, nb = 8 with a block write) under the
+same protocol and reports each in `workloads`.
 
-Protocol:
+Protocol, per workload:
   * L distinct layer copies (W, x, prefix, blocks, out, aux, workspace) with a
     footprint of at least 640 MB, so the 256 MB Infinity Cache cannot serve W;
-    copy 0 is checked against the FP64 oracle before timing.
+    the first call on copy 0 is checked against the FP64 oracle before timing
+    (new prefix within one projection ulp, output within two bf16 ulps of the
+    oracle's AttnRes on the GPU's own new prefix).
   * `--warmup` eager steps, then one HIP graph holding exactly `--steps` calls
     that cycle through the copies; the graph is replayed once untimed (upload)
     and once timed, bracketed by synchronisations and HIP events on the stream
-    the kernels run on.
+    the kernels run on. Afterwards every copy's workspace is checked (a wait
+    that gave up would invalidate the results and fails the run).
   * value = algorithmic bytes per step / measured time per step (GB/s);
     roofline.achieved is the same figure for the fused kernel, the only kernel
     of a step, against the 8 TB/s HBM peak.
-  * cpu_baseline: the FP64 oracle (oracle/, plain C) on the same step, timed on
-    the host cores, in the same process.
+  * cpu_baseline: the FP64 oracle (oracle/, plain C) on the headline step,
+    timed on one host thread and on every core the process may use, in the
+    same process.
 
-Prints one JSON line. `--config` picks another fused workload (0: M=1 K=1024
-nb=1; 2: M=64 K=8192 nb=8 with a block write) for side measurements; `--config
-3` (attnres_run, T=256, nb = 0..8, final boundary), `--config 4`
-(wsgemm_run, K=7168, N=4096, M = 1, 8, 16, 48, 64; beyond 32 tokens also
-wsgemm_run_ws, which alone takes M = 128; at M = 8 and 64 also the MoE-front
-epilogue) and `--config 5`
+Prints one JSON line. `--config` picks another headline among the fused
+workloads (0, 1, 2; `--only` times just that one); `--config 3` (attnres_run,
+T=256, nb = 0..8, final boundary), `--config 4` (wsgemm_run, K=7168, N=4096,
+M = 1, 8, 16, 48, 64; beyond 32 tokens also wsgemm_run_ws, which alone takes
+M = 128; at M = 8 and 64 also the MoE-front epilogue) and `--config 5`
 (look-ahead statistics: attnres_oproj_ahead_run beside attnres_oproj_run on
 workloads 0-2, attnres_post_run beside attnres_run at T=256, nb=8) print one
 JSON line per case, timed the same way.
@@ -326,15 +332,139 @@ def lookahead_configs(args, np, torch, sga, synth, up, steps):
               f"{name} T={T} H={H} nb={nb} final=1 aux=1", layer_copies=L)
 
 
+def fused_measure(cfg_id, args, np, torch, sga, synth, dev, final=0):
+    """One fused workload: parity of the first call on copy 0 against the
+    oracle, then `steps` calls in one HIP graph, timed. Every layer copy's
+    workspace is checked after the timed replay (a wait that gave up would
+    make the results invalid). Returns the workload's figures and inputs."""
+    cfg = WORKLOADS[cfg_id]
+    M, K, nb, cap, write, has_delta = (cfg[k] for k in ("M", "K", "nb", "cap", "write",
+                                                      "has_delta"))
+    s = synth.decode_step(M, K, nb, cap=cap, write=write, has_delta=has_delta, final=final,
+                          seed=0)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    step_bytes = algorithmic_bytes(M, K, nb, write, has_delta)
+    copy_bytes = 2 * H * K + 2 * M * K + M * 2 * H * (4 + cap)
+    L = max(2, math.ceil(FOOTPRINT / copy_bytes))
+    base = dict(x=up(s.x), W=up(s.W), prefix=up(s.prefix), blocks=up(s.blocks))
+    norm, query, out_norm = up(s.norm), up(s.query), up(s.out_norm)
+    layers = []
+    for i in range(L):
+        t = {k: v.clone() for k, v in base.items()}
+        t["out"] = torch.zeros((M, H), dtype=torch.int16, device=dev)
+        t["aux"] = torch.zeros((M, H), dtype=torch.int16, device=dev)
+        t["ws"] = sga.make_workspace(M, H, nb, dev)
+        layers.append(t)
+    del base
+    torch.cuda.synchronize()
+
+    def step(i):
+        t = layers[i % L]
+        sga.attnres_oproj_run(t["x"], t["W"], t["prefix"], t["blocks"], norm, query, out_norm,
+                              t["out"], t["aux"], t["ws"], nb=nb, write=write,
+                              has_delta=has_delta, final_boundary=final)
+
+    if not args.no_check:
+        # the first call on copy 0 (fresh inputs) against the oracle: the new
+        # prefix within one projection ulp, the output within two bf16 ulps
+        # of the oracle's AttnRes on the GPU's own new prefix
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from parity_tools import check_fused_step
+
+        step(0)
+        torch.cuda.synchronize()
+        sga.check_workspace(layers[0]["ws"])
+
+        def down(t):
+            return t.cpu().numpy().view(np.uint16)
+
+        check_fused_step(x=s.x, W=s.W, old_prefix=s.prefix, blocks=s.blocks, norm=s.norm,
+                         query=s.query, out_norm=s.out_norm, nb=nb, write=write,
+                         has_delta=has_delta, final=final, eps=s.eps, out_eps=s.out_eps,
+                         gpu_out=down(layers[0]["out"]), gpu_new=down(layers[0]["prefix"]),
+                         what=f"bench config {cfg_id}", nthreads=len(os.sched_getaffinity(0)))
+
+    us_step = graph_time_us(torch, step, args.steps, args.warmup)
+    for t in layers:  # every copy: no wait gave up during the timed replays
+        sga.check_workspace(t["ws"])
+    del layers
+    torch.cuda.empty_cache()
+    gbs = step_bytes / (us_step * 1e-6) / 1e9
+    rec = MEASURED_TRAFFIC.get(cfg_id)
+    traffic = None
+    if rec is not None and final == 0 and rec["digest"] == kernel_digest():
+        traffic = rec["fetch"] + rec["write"]
+    fig = {
+        "workload": f"fused o-proj + AttnRes, M={M}, K={K}, N=H={H}, nb={nb}, "
+                    f"write={write}, has_delta={has_delta}, aux=1, final={final}",
+        "M": M, "K": K, "nb": nb, "write": write,
+        "us_per_layer_step": round(us_step, 3),
+        "achieved_GBs": round(gbs, 1),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1),
+        "frac": round(gbs / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_launch": step_bytes,
+        "traffic": traffic,
+        "layer_copies": L, "footprint_MB": round(L * copy_bytes / 1e6, 1),
+    }
+    return fig, s
+
+
+def cpu_baseline(args, np, s, cfg_id, final):
+    """The FP64 oracle on the same step (copy 0 of the inputs), timed twice on
+    the host: one thread, then every core this process may run on (the oracle
+    splits the GEMM over output elements and AttnRes over tokens, with the
+    same bits either way). Each leg runs for about `--cpu-seconds`."""
+    import oracle
+
+    cfg = WORKLOADS[cfg_id]
+    M, K, nb, write, has_delta = (cfg[k] for k in ("M", "K", "nb", "write", "has_delta"))
+    step_bytes = algorithmic_bytes(M, K, nb, write, has_delta)
+    cores = len(os.sched_getaffinity(0))
+
+    def leg(threads):
+        times = []
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            oracle.attnres_oproj(s.x, s.W, s.prefix, s.blocks, s.norm, s.query, s.out_norm,
+                                 nb=nb, write=write, has_delta=has_delta, final=final,
+                                 nthreads=threads)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start >= args.cpu_seconds or len(times) >= 200:
+                break
+        return float(np.median(times)), len(times)
+
+    t_all, n_all = leg(cores)
+    t_one, n_one = leg(1)
+    return {
+        "value": round(step_bytes / t_all / 1e9, 3),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{n_all} full steps of the headline workload (config {cfg_id}, copy 0) on "
+                  f"{cores} threads, median {t_all * 1e3:.2f} ms/step; {n_one} steps on one "
+                  f"thread, median {t_one * 1e3:.2f} ms/step; FP64 C oracle (GEMM split over "
+                  f"output elements, AttnRes over tokens)",
+        "ms_per_step": round(t_all * 1e3, 3),
+        "single_thread": {"value": round(step_bytes / t_one / 1e9, 3), "unit": "GB/s",
+                          "cores": 1, "ms_per_step": round(t_one * 1e3, 3)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, choices=sorted(WORKLOADS) + [3, 4, 5])
+    ap.add_argument("--only", action="store_true",
+                    help="time only --config (the default run times configs 0, 1 and 2)")
     ap.add_argument("--final", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="bounded host time for the oracle baseline (0 skips it)")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="bounded host time per leg of the oracle baseline (0 skips it)")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--stream-read-gb", type=float, default=2.0,
                     help="size of the streaming-read reference measurement (0: skip)")
@@ -356,59 +486,8 @@ def main():
         side_configs(args, np, torch, sga, synth)
         return
 
-    cfg = WORKLOADS[args.config]
-    M, K, nb, cap, write, has_delta = (cfg[k] for k in ("M", "K", "nb", "cap", "write",
-                                                      "has_delta"))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    s = synth.decode_step(M, K, nb, cap=cap, write=write, has_delta=has_delta,
-                          final=args.final, seed=0)
-
-    def up(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
-
-    step_bytes = algorithmic_bytes(M, K, nb, write, has_delta)
-    copy_bytes = 2 * H * K + 2 * M * K + M * 2 * H * (4 + cap)
-    L = max(2, math.ceil(FOOTPRINT / copy_bytes))
-    base = dict(x=up(s.x), W=up(s.W), prefix=up(s.prefix), blocks=up(s.blocks))
-    norm, query, out_norm = up(s.norm), up(s.query), up(s.out_norm)
-    layers = []
-    for i in range(L):
-        t = {k: v.clone() for k, v in base.items()}
-        t["out"] = torch.zeros((M, H), dtype=torch.int16, device=dev)
-        t["aux"] = torch.zeros((M, H), dtype=torch.int16, device=dev)
-        t["ws"] = sga.make_workspace(M, H, nb, dev)
-        layers.append(t)
-    torch.cuda.synchronize()
-
-    def step(i):
-        t = layers[i % L]
-        sga.attnres_oproj_run(t["x"], t["W"], t["prefix"], t["blocks"], norm, query, out_norm,
-                              t["out"], t["aux"], t["ws"], nb=nb, write=write,
-                              has_delta=has_delta, final_boundary=args.final)
-
-    # parity of the first call on copy 0 (fresh inputs) against the oracle
-    if not args.no_check:
-        import oracle
-
-        sys.path.insert(0, os.path.join(ROOT, "tests"))
-        from parity_tools import assert_new_prefix_close
-
-        step(0)
-        torch.cuda.synchronize()
-        ref = oracle.attnres_oproj(s.x, s.W, s.prefix, s.blocks, s.norm, s.query, s.out_norm,
-                                   nb=nb, write=write, has_delta=has_delta, final=args.final,
-                                   nthreads=8)
-        got_prefix = layers[0]["prefix"].cpu().numpy().view(np.uint16)
-        assert_new_prefix_close(got_prefix, ref.prefix, s.prefix, has_delta, "bench prefix")
-        o = synth.bf16_bits_to_f32(layers[0]["out"].cpu().numpy().view(np.uint16))
-        r = synth.bf16_bits_to_f32(ref.out)
-        rel = float(np.linalg.norm(o - r) / np.linalg.norm(r))
-        assert rel < 5e-3, f"bench parity: relative L2 {rel}"
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
 
     if args.calibrate_copy_mb > 0:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give
@@ -422,68 +501,51 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    stream = torch.cuda.Stream()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(args.steps):
-                step(i)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        graph.replay()  # upload / first-launch costs, untimed
-    torch.cuda.synchronize()
-
-    with torch.cuda.stream(stream):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        graph.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    us_step = ms_total * 1e3 / args.steps
-    gbs = step_bytes / (us_step * 1e-6) / 1e9
-
-    rec = MEASURED_TRAFFIC.get(args.config)
-    traffic = None
-    if rec is not None and args.final == 0 and rec["digest"] == kernel_digest():
-        traffic = rec["fetch"] + rec["write"]
+    head = args.config
+    order = [head] if args.only else [head] + [c for c in sorted(WORKLOADS) if c != head]
+    figs, inputs = {}, {}
+    for c in order:
+        figs[c], inputs[c] = fused_measure(c, args, np, torch, sga, synth, dev, final=args.final)
+    f = figs[head]
+    us_step = f["us_per_layer_step"]
+    gbs = f["achieved_GBs"]
 
     result = {
         "metric": "µs/layer-step + achieved HBM GB/s (% of peak), o-proj+AttnRes, M=1/8/64",
-        "value": round(gbs, 1),
+        "value": gbs,
         "unit": "GB/s",
-        "us_per_layer_step": round(us_step, 3),
-        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1),
+        "us_per_layer_step": us_step,
+        "pct_of_hbm_peak": f["pct_of_hbm_peak"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_total / args.steps, 6),
+        "ms_per_step": round(us_step / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded SplitMix64 normals, bf16)",
         "config": {
-            "workload": f"fused o-proj + AttnRes, M={M}, K={K}, N=H={H}, nb={nb}, "
-                        f"write={write}, has_delta={has_delta}, aux=1, final={args.final}",
-            "M": M, "K": K, "N": H, "nb": nb, "write": write, "final": args.final,
-            "layer_copies": L, "footprint_MB": round(L * copy_bytes / 1e6, 1),
-            "timing": "one HIP graph of `steps` calls, HIP events on the launch stream",
+            "workload": f["workload"],
+            "M": f["M"], "K": f["K"], "N": H, "nb": f["nb"], "write": f["write"],
+            "final": args.final, "layer_copies": f["layer_copies"],
+            "footprint_MB": f["footprint_MB"],
+            "timing": "one HIP graph of `steps` calls per workload, HIP events on the launch "
+                      "stream; every workspace checked after the timed replay",
         },
         "roofline": {
             "bound": "hbm",
-            "achieved": round(gbs, 1),
+            "achieved": gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
+            "frac": f["frac"],
+            "traffic": f["traffic"],
             "kernel": "fused_kernel (attnres_oproj_run), one launch per step",
-            "algorithmic_bytes_per_launch": step_bytes,
+            "algorithmic_bytes_per_launch": f["algorithmic_bytes_per_launch"],
             "traffic_note": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated); "
                             "null unless measured on these kernel sources",
         },
+        "workloads": [figs[c] for c in sorted(figs)],
     }
 
     if args.stream_read_gb > 0:
@@ -492,33 +554,11 @@ def main():
         rd = stream_read_gbs(torch, sga, dev, args.stream_read_gb)
         result["stream_read"] = rd
         result["pct_of_measured_read_bw"] = round(100.0 * gbs / rd["gbs"], 1)
+        for w in result["workloads"]:
+            w["pct_of_measured_read_bw"] = round(100.0 * w["achieved_GBs"] / rd["gbs"], 1)
 
     if args.cpu_seconds > 0:
-        import oracle
-
-        cores = len(os.sched_getaffinity(0))
-        threads = min(cores, M)
-        times = []
-        t_start = time.perf_counter()
-        while True:
-            t0 = time.perf_counter()
-            oracle.attnres_oproj(s.x, s.W, s.prefix, s.blocks, s.norm, s.query, s.out_norm,
-                                 nb=nb, write=write, has_delta=has_delta, final=args.final,
-                                 nthreads=threads)
-            times.append(time.perf_counter() - t0)
-            if time.perf_counter() - t_start >= args.cpu_seconds or len(times) >= 200:
-                break
-        t_med = float(np.median(times))
-        result["cpu_baseline"] = {
-            "value": round(step_bytes / t_med / 1e9, 3),
-            "unit": "GB/s",
-            "cores": threads,
-            "kind": "oracle",
-            "sample": f"{len(times)} full steps of the same workload (copy 0), median "
-                      f"{t_med * 1e3:.1f} ms/step, FP64 C oracle with {threads} threads "
-                      f"(one per token) of {cores} available",
-            "ms_per_step": round(t_med * 1e3, 2),
-        }
+        result["cpu_baseline"] = cpu_baseline(args, np, inputs[head], head, args.final)
     print(json.dumps(result), flush=True)
 
 
