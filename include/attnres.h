@@ -199,7 +199,9 @@ int attnres_oproj_workspace_init(void* workspace, size_t workspace_bytes, void* 
  * (attnres_oproj_run, attnres_oproj_ahead_run, wsgemm_run_ws) gave up: waits
  * until the work enqueued on `stream` so far has finished (it synchronises
  * the host with the stream; not for use under stream capture), then reads the
- * workspace header.
+ * workspace header. workspace == NULL with workspace_bytes == 0 names the
+ * current device's array of attnres_oproj_run_noalloc (ATTNRES_OK if no call
+ * has used it).
  * Returns ATTNRES_OK (no wait gave up: the outputs of every call so far are
  * valid), ATTNRES_EWAIT (a wait gave up: see attnres_oproj_workspace_init),
  * ATTNRES_EWORKSPACE (NULL, fewer than 256 bytes or not 256-byte aligned) or
@@ -227,6 +229,35 @@ int attnres_oproj_run(const void* x, int64_t ldx, const void* W, int64_t ldw, in
                       const void* out_norm, void* out, int64_t ld_out, void* aux, int64_t ld_aux,
                       float eps, float out_eps, int M, int H, int nb, int write, int has_delta,
                       int final_boundary, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attnres_oproj_run_noalloc - attnres_oproj_run without a caller workspace,
+ * for callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation). It allocates
+ * nothing: its workspace is a device array inside the library, one per
+ * device, ATTNRES_NOALLOC_WORKSPACE_BYTES (the largest workspace
+ * attnres_oproj_run needs: 64 tokens of 8192 columns), held until the
+ * process ends. The first call on a device looks the array up and enqueues
+ * one small kernel that arms it, ahead of the step on `stream`. Every
+ * argument means what it means for attnres_oproj_run, which gives the same
+ * bits; sizes beyond the array (none within the limits of attnres_oproj_run)
+ * return ATTNRES_EWORKSPACE.
+ * Every call on a device shares that device's array, which each call leaves
+ * armed for the next: calls that may overlap on one device (other streams,
+ * other threads, graph replays running beside eager calls) race and must be
+ * ordered by the caller. `stream` must belong to the current device
+ * (ATTNRES_EINVAL otherwise). attnres_workspace_status(NULL, 0, stream)
+ * reports whether a wait of a call on the current device's array gave up;
+ * the array then stays flagged (later calls write nothing) until the process
+ * ends.
+ */
+#define ATTNRES_NOALLOC_WORKSPACE_BYTES 3145984
+int attnres_oproj_run_noalloc(const void* x, int64_t ldx, const void* W, int64_t ldw, int K,
+                              void* prefix, int64_t ld_prefix, void* blocks, int64_t blk_stride_t,
+                              int64_t blk_stride_b, int cap, const void* norm, const void* query,
+                              const void* out_norm, void* out, int64_t ld_out, void* aux,
+                              int64_t ld_aux, float eps, float out_eps, int M, int H, int nb,
+                              int write, int has_delta, int final_boundary, void* stream);
 
 /*
  * attnres_oproj_ahead_run - attnres_oproj_run that also stores the saved-block

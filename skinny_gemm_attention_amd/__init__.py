@@ -43,6 +43,9 @@ _lib.attnres_oproj_workspace_init.restype = _I
 _lib.attnres_oproj_run.argtypes = [_P, _I64, _P, _I64, _I, _P, _I64, _P, _I64, _I64, _I, _P, _P,
                                    _P, _P, _I64, _P, _I64, _F, _F, _I, _I, _I, _I, _I, _I, _P,
                                    _SZ, _P]
+_lib.attnres_oproj_run_noalloc.argtypes = [_P, _I64, _P, _I64, _I, _P, _I64, _P, _I64, _I64, _I,
+                                           _P, _P, _P, _P, _I64, _P, _I64, _F, _F, _I, _I, _I, _I,
+                                           _I, _I, _P]
 _lib.attnres_oproj_ahead_run.argtypes = [_P, _I64, _P, _I64, _I, _P, _I64, _P, _I64, _I64, _I,
                                          _P, _P, _P, _P, _I64, _P, _I64, _F, _F, _I, _I, _I, _I,
                                          _I, _I, _P, _P, _F, _P, _I64, _P, _P, _SZ, _P]
@@ -55,7 +58,7 @@ _lib.attnres_stream_read.restype = _I
 _lib.attnres_strerror.argtypes = [_I]
 _lib.attnres_strerror.restype = ctypes.c_char_p
 for _f in (_lib.attnres_run, _lib.wsgemm_run, _lib.wsgemm_run_ws, _lib.wsgemm_moe_front_run,
-           _lib.attnres_oproj_run,
+           _lib.attnres_oproj_run, _lib.attnres_oproj_run_noalloc,
            _lib.attnres_oproj_ahead_run, _lib.attnres_post_run):
     _f.restype = _I
 
@@ -63,7 +66,8 @@ EXPORTS = ("attnres_run", "wsgemm_run", "wsgemm_moe_front_run", "wsgemm_workspac
            "wsgemm_run_ws",
            "attnres_oproj_run", "attnres_oproj_workspace_size",
            "attnres_oproj_workspace_init", "attnres_oproj_ahead_run", "attnres_post_run",
-           "attnres_strerror", "attnres_stream_read", "attnres_workspace_status")
+           "attnres_strerror", "attnres_stream_read", "attnres_workspace_status",
+           "attnres_oproj_run_noalloc")
 
 STREAM_READ_SINK_WORDS = 65536  # ATTNRES_STREAM_READ_SINK_WORDS
 EWAIT = -7  # ATTNRES_EWAIT: a wait of an earlier call on the workspace gave up
@@ -254,10 +258,13 @@ def attnres_workspace_status(workspace, stream=None) -> int:
     """Waits for the work enqueued on the stream, then returns 0 when no wait of
     a call on this workspace gave up, EWAIT when one did (that call's outputs
     are invalid and later calls write nothing until the workspace is re-armed
-    by attnres_oproj_workspace_init)."""
-    rc = _lib.attnres_workspace_status(ctypes.c_void_p(workspace.data_ptr()),
-                                       workspace.numel() * workspace.element_size(),
-                                       _stream(stream))
+    by attnres_oproj_workspace_init). workspace=None: the library's own array
+    of attnres_oproj_run_noalloc on the current device."""
+    if workspace is None:
+        ptr, nbytes = None, 0
+    else:
+        ptr, nbytes = ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+    rc = _lib.attnres_workspace_status(ptr, nbytes, _stream(stream))
     if rc not in (0, EWAIT):
         raise AttnResError(rc, "attnres_workspace_status")
     return rc
@@ -312,6 +319,25 @@ def attnres_oproj_run(x, W, prefix, blocks, norm, query, out_norm, out, aux, wor
                                 _ptr(aux), _row_stride(aux), eps, out_eps, M, H, nb, write,
                                 int(has_delta), int(final_boundary), ws, wsb, _stream(stream))
     _check(rc, "attnres_oproj_run")
+    return out, prefix, blocks
+
+
+def attnres_oproj_run_noalloc(x, W, prefix, blocks, norm, query, out_norm, out, aux, *, nb,
+                              write=-1, has_delta=1, final_boundary=0, eps=1e-6, out_eps=1e-6,
+                              stream=None):
+    """attnres_oproj_run with the library's own workspace (no allocation by the
+    library or here); calls that overlap on one device race."""
+    M, K = x.shape
+    H = W.shape[0]
+    _rows(W, H, K, "W")
+    _attn_shapes(M, H, prefix, blocks, norm, query, out_norm, out, aux)
+    bst_t, bst_b, cap = _block_strides(blocks)
+    rc = _lib.attnres_oproj_run_noalloc(
+        _ptr(x), _row_stride(x), _ptr(W), _row_stride(W), K, _ptr(prefix), _row_stride(prefix),
+        _ptr(blocks), bst_t, bst_b, cap, _ptr(norm), _ptr(query), _ptr(out_norm), _ptr(out),
+        _row_stride(out), _ptr(aux), _row_stride(aux), eps, out_eps, M, H, nb, write,
+        int(has_delta), int(final_boundary), _stream(stream))
+    _check(rc, "attnres_oproj_run_noalloc")
     return out, prefix, blocks
 
 

@@ -5,6 +5,8 @@
 #include "../../include/attnres.h"
 #include "launch.hpp"
 
+#include <mutex>
+
 namespace attnres {
 // stream_read.hip: reads `bytes` (a multiple of 16) at src once; workgroup
 // g < grid stores the XOR of the words it read to sink[g].
@@ -241,12 +243,89 @@ int attnres_oproj_workspace_init(void* workspace, size_t workspace_bytes, void* 
 
 namespace {
 
+// ---- the library's own workspace (attnres_oproj_run_noalloc) -----------------
+//
+// For callers that cannot allocate, the workspace of attnres_oproj_run lives
+// in a file-scope device array, one copy per device, held until the process
+// ends: the largest workspace the fused call can need (64 tokens, H = 8192;
+// 3,145,984 bytes). On the host, `scratch` is only a stand-in for the device
+// copies: its address on a device comes from hipGetSymbolAddress, looked up
+// once per device with that device current, and only that address is ever
+// handed to a kernel or a copy.
+constexpr size_t kStaticWorkspaceBytes = attnres::kWorkspaceHeader +
+                                         (size_t)ATTNRES_MAX_M * ATTNRES_MAX_H * 2 +
+                                         attnres::split_partial_bytes(ATTNRES_MAX_M, ATTNRES_MAX_H);
+static_assert(kStaticWorkspaceBytes == ATTNRES_NOALLOC_WORKSPACE_BYTES, "header figure");
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+
+constexpr int kMaxDevices = 64;
+struct StaticWorkspace {
+  void* ptr = nullptr;  // device address of `scratch` on this device
+  bool armed = false;   // an arming kernel has run (not merely been captured) on it
+};
+std::mutex g_static_mu;
+StaticWorkspace g_static[kMaxDevices];
+
+// The device `stream` belongs to, which must be the current device.
+int stream_device(hipStream_t stream, int* dev) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return ATTNRES_EHIP;
+  if (stream) {
+    hipDevice_t sd = 0;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return ATTNRES_EHIP;
+    if ((int)sd != cur) return ATTNRES_EINVAL;
+  }
+  if (cur < 0 || cur >= kMaxDevices) return ATTNRES_EINVAL;
+  *dev = cur;
+  return ATTNRES_OK;
+}
+
+// The current device's copy of `scratch`, armed before its first use: the
+// arming kernel is enqueued on `stream` ahead of the call that needs it. When
+// `stream` is being captured, the arming kernel goes into the graph (every
+// replay re-arms the array, which is harmless) and the device still counts
+// as unarmed, so the next call outside a capture arms it again.
+int static_workspace(hipStream_t stream, void** ws) {
+  int dev = 0;
+  int rc = stream_device(stream, &dev);
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticWorkspace& st = g_static[dev];
+  if (!st.ptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATTNRES_EHIP;
+    st.ptr = p;
+  }
+  if (!st.armed) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return ATTNRES_EHIP;
+    if (attnres::launch_workspace_init(st.ptr, kStaticWorkspaceBytes, stream) != hipSuccess)
+      return ATTNRES_EHIP;
+    if (cs == hipStreamCaptureStatusNone) st.armed = true;
+  }
+  *ws = st.ptr;
+  return ATTNRES_OK;
+}
+
+// The current device's copy of `scratch` if a call has used it, else nullptr.
+int static_workspace_if_used(hipStream_t stream, void** ws) {
+  int dev = 0;
+  int rc = stream_device(stream, &dev);
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  *ws = g_static[dev].ptr;
+  return ATTNRES_OK;
+}
+
+// Checks and launch of the fused call; with `library_ws` the workspace is the
+// library's own (attnres_oproj_run_noalloc) and `workspace` is ignored.
 int oproj_common(const void* x, int64_t ldx, const void* W, int64_t ldw, int K, void* prefix,
                  int64_t ld_prefix, void* blocks, int64_t blk_stride_t, int64_t blk_stride_b,
                  int cap, const void* norm, const void* query, const void* out_norm, void* out,
                  int64_t ld_out, void* aux, int64_t ld_aux, float eps, float out_eps, int M, int H,
                  int nb, int write, int has_delta, int final_boundary, void* workspace,
-                 size_t workspace_bytes, const attnres::AheadParams& ah, void* stream) {
+                 size_t workspace_bytes, const attnres::AheadParams& ah, void* stream,
+                 bool library_ws = false) {
   int rc = check_attnres(prefix, ld_prefix, blocks, blk_stride_t, blk_stride_b, cap, norm, query,
                          out_norm, out, ld_out, aux, ld_aux, eps, out_eps, M, H, nb, write,
                          has_delta, final_boundary);
@@ -257,6 +336,14 @@ int oproj_common(const void* x, int64_t ldx, const void* W, int64_t ldw, int K, 
   if (K > 0 && (ldx < K || ldw < K)) return ATTNRES_EINVAL;
   if (K > 0 && (!aligned16(x) || !aligned16(W))) return ATTNRES_EALIGN;
   if (K > 0 && (!stride8(ldx) || !stride8(ldw))) return ATTNRES_EALIGN;
+  if (library_ws) {
+    // never reached within the limits above: the array covers 64 tokens of
+    // the widest rows
+    if (workspace_bytes_for(M, H) > kStaticWorkspaceBytes) return ATTNRES_EWORKSPACE;
+    rc = static_workspace(static_cast<hipStream_t>(stream), &workspace);
+    if (rc) return rc;
+    workspace_bytes = kStaticWorkspaceBytes;
+  }
   if (!workspace || workspace_bytes < workspace_bytes_for(M, H) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return ATTNRES_EWORKSPACE;
@@ -294,6 +381,18 @@ int attnres_oproj_run(const void* x, int64_t ldx, const void* W, int64_t ldw, in
                       cap, norm, query, out_norm, out, ld_out, aux, ld_aux, eps, out_eps, M, H,
                       nb, write, has_delta, final_boundary, workspace, workspace_bytes, ah,
                       stream);
+}
+
+int attnres_oproj_run_noalloc(const void* x, int64_t ldx, const void* W, int64_t ldw, int K,
+                              void* prefix, int64_t ld_prefix, void* blocks, int64_t blk_stride_t,
+                              int64_t blk_stride_b, int cap, const void* norm, const void* query,
+                              const void* out_norm, void* out, int64_t ld_out, void* aux,
+                              int64_t ld_aux, float eps, float out_eps, int M, int H, int nb,
+                              int write, int has_delta, int final_boundary, void* stream) {
+  attnres::AheadParams ah = {nullptr, nullptr, 0.0f, nullptr, 0, nullptr};
+  return oproj_common(x, ldx, W, ldw, K, prefix, ld_prefix, blocks, blk_stride_t, blk_stride_b,
+                      cap, norm, query, out_norm, out, ld_out, aux, ld_aux, eps, out_eps, M, H,
+                      nb, write, has_delta, final_boundary, nullptr, 0, ah, stream, true);
 }
 
 int attnres_oproj_ahead_run(const void* x, int64_t ldx, const void* W, int64_t ldw, int K,
@@ -356,10 +455,18 @@ int attnres_post_run(const void* delta, int64_t ld_delta, void* prefix, int64_t 
 }
 
 int attnres_workspace_status(const void* workspace, size_t workspace_bytes, void* stream) {
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!workspace && workspace_bytes == 0) {  // the library's own (attnres_oproj_run_noalloc)
+    void* own = nullptr;
+    const int rc = static_workspace_if_used(s, &own);
+    if (rc) return rc;
+    if (!own) return ATTNRES_OK;  // no call has used it on this device
+    workspace = own;
+    workspace_bytes = kStaticWorkspaceBytes;
+  }
   if (!workspace || workspace_bytes < attnres::kWorkspaceHeader ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return ATTNRES_EWORKSPACE;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
   unsigned word = 0;
   if (hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)

@@ -32,7 +32,7 @@ constexpr unsigned kMailboxSentinel = 0x80000000u;
 constexpr size_t kWorkspaceHeader = 256;
 
 // Split-K hand-off bytes for M tokens and H rows (0 when no split is used).
-inline size_t split_partial_bytes(int M, int H) {
+constexpr size_t split_partial_bytes(int M, int H) {
   if (M <= 32) return 0;
   const size_t groups = (size_t)(H + 63) / 64;
   const size_t quads = 4 * (size_t)((M + 15) / 16) * 64;  // four row tiles x token tiles

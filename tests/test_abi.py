@@ -38,6 +38,8 @@ def lib():
                                           P, SZ, P]
     L.attnres_post_run.argtypes = [P, I64, P, I64, P, I64, I64, I, P, P, P, P, I64, P, I64, P, I64,
                                    P, F, F, I, I, I, I, I, I, P]
+    L.attnres_oproj_run_noalloc.argtypes = [P, I64, P, I64, I, P, I64, P, I64, I64, I, P, P, P,
+                                            P, I64, P, I64, F, F, I, I, I, I, I, I, P]
     L.attnres_workspace_status.argtypes = [P, SZ, P]
     L.attnres_workspace_status.restype = I
     L.attnres_stream_read.argtypes = [P, SZ, P, P]
@@ -59,7 +61,8 @@ def test_header_symbols_exported(lib):
                           "attnres_oproj_workspace_size",
                           "attnres_oproj_workspace_init", "attnres_oproj_run",
                           "attnres_oproj_ahead_run", "attnres_post_run", "attnres_strerror",
-                          "attnres_stream_read", "attnres_workspace_status"}
+                          "attnres_stream_read", "attnres_workspace_status",
+                          "attnres_oproj_run_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -166,6 +169,34 @@ def call_fused(lib, **kw):
 ])
 def test_attnres_oproj_run_rejects(lib, change, code):
     assert call_fused(lib, **change) == code
+
+
+def call_noalloc(lib, **kw):
+    a = attn_args()
+    a.update(x=A, ldx=8192, W=A, ldw=8192, K=8192, M=4)
+    a.update(kw)
+    return lib.attnres_oproj_run_noalloc(
+        a["x"], a["ldx"], a["W"], a["ldw"], a["K"], a["prefix"], a["ld_prefix"], a["blocks"],
+        a["bst_t"], a["bst_b"], a["cap"], a["norm"], a["query"], a["out_norm"], a["out"],
+        a["ld_out"], a["aux"], a["ld_aux"], a["eps"], a["out_eps"], a["M"], a["H"], a["nb"],
+        a["write"], a["has_delta"], a["final"], None)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(x=None), -1), (dict(W=None), -1), (dict(M=0), -3), (dict(M=65), -3), (dict(K=8190), -4),
+    (dict(ldx=4096), -1), (dict(W=A + 8), -2), (dict(nb=9, cap=10, bst_t=10 * H), -3),
+    (dict(H=100), -4), (dict(H=8200), -4), (dict(prefix=None), -1),
+])
+def test_attnres_oproj_run_noalloc_rejects(lib, change, code):
+    """Every argument is checked before the library's array is looked up or
+    armed (no HIP call is made by any case here)."""
+    assert call_noalloc(lib, **change) == code
+
+
+def test_noalloc_array_covers_every_fused_workspace(lib):
+    m = re.search(r"#define ATTNRES_NOALLOC_WORKSPACE_BYTES (\d+)", open(HEADER).read())
+    biggest = lib.attnres_oproj_workspace_size(64, 8192, 8)
+    assert m and int(m.group(1)) == biggest == 3_145_984
 
 
 def call_ahead(lib, **kw):
