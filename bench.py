@@ -56,11 +56,7 @@ FOOTPRINT = 640e6
 # code (comments and whitespace aside), and roofline.traffic is null when the
 # sources differ.
 KERNEL_SOURCES = ("common.hpp", "token.hpp", "gemm.hpp", "launch.hpp", "fused.hip")
-MEASURED_TRAFFIC = {
-    1: {"digest": "531aafd4eec435f5cd94eb0b8557dc07d5d3a7fb06a70d512318039e2d75af71", "fetch": 60981881, "write": 991400},
-    0: {"digest": "531aafd4eec435f5cd94eb0b8557dc07d5d3a7fb06a70d512318039e2d75af71", "fetch": 14932957, "write": 123390},
-    2: {"digest": "531aafd4eec435f5cd94eb0b8557dc07d5d3a7fb06a70d512318039e2d75af71", "fetch": 139224343, "write": 9175040},
-}
+MEASURED_TRAFFIC = {}  # (workload, "prepared" | "row-major") -> {"digest", "fetch", "write"}
 
 WORKLOADS = {
     0: dict(M=1, K=1024, nb=1, cap=1, write=-1, has_delta=1),
@@ -332,11 +328,14 @@ def lookahead_configs(args, np, torch, sga, synth, up, steps):
               f"{name} T={T} H={H} nb={nb} final=1 aux=1", layer_copies=L)
 
 
-def fused_measure(cfg_id, args, np, torch, sga, synth, dev, final=0):
+def fused_measure(cfg_id, args, np, torch, sga, synth, dev, final=0, packed=False):
     """One fused workload: parity of the first call on copy 0 against the
     oracle, then `steps` calls in one HIP graph, timed. Every layer copy's
     workspace is checked after the timed replay (a wait that gave up would
-    make the results invalid). Returns the workload's figures and inputs."""
+    make the results invalid). With `packed` each copy's W is prepared once
+    (attnres_pack_weights, outside the timed region, as a layer binds its
+    weight when it is prepared) and the step is attnres_oproj_packed_run.
+    Returns the workload's figures and inputs."""
     cfg = WORKLOADS[cfg_id]
     M, K, nb, cap, write, has_delta = (cfg[k] for k in ("M", "K", "nb", "cap", "write",
                                                       "has_delta"))
@@ -354,6 +353,8 @@ def fused_measure(cfg_id, args, np, torch, sga, synth, dev, final=0):
     layers = []
     for i in range(L):
         t = {k: v.clone() for k, v in base.items()}
+        if packed:
+            t["W"] = sga.attnres_pack_weights(t["W"])
         t["out"] = torch.zeros((M, H), dtype=torch.int16, device=dev)
         t["aux"] = torch.zeros((M, H), dtype=torch.int16, device=dev)
         t["ws"] = sga.make_workspace(M, H, nb, dev)
@@ -363,9 +364,14 @@ def fused_measure(cfg_id, args, np, torch, sga, synth, dev, final=0):
 
     def step(i):
         t = layers[i % L]
-        sga.attnres_oproj_run(t["x"], t["W"], t["prefix"], t["blocks"], norm, query, out_norm,
-                              t["out"], t["aux"], t["ws"], nb=nb, write=write,
-                              has_delta=has_delta, final_boundary=final)
+        if packed:
+            sga.attnres_oproj_packed_run(t["x"], t["W"], H, t["prefix"], t["blocks"], norm, query,
+                                         out_norm, t["out"], t["aux"], t["ws"], nb=nb,
+                                         write=write, has_delta=has_delta, final_boundary=final)
+        else:
+            sga.attnres_oproj_run(t["x"], t["W"], t["prefix"], t["blocks"], norm, query,
+                                  out_norm, t["out"], t["aux"], t["ws"], nb=nb, write=write,
+                                  has_delta=has_delta, final_boundary=final)
 
     if not args.no_check:
         # the first call on copy 0 (fresh inputs) against the oracle: the new
@@ -393,14 +399,15 @@ def fused_measure(cfg_id, args, np, torch, sga, synth, dev, final=0):
     del layers
     torch.cuda.empty_cache()
     gbs = step_bytes / (us_step * 1e-6) / 1e9
-    rec = MEASURED_TRAFFIC.get(cfg_id)
+    rec = MEASURED_TRAFFIC.get((cfg_id, "prepared" if packed else "row-major"))
     traffic = None
     if rec is not None and final == 0 and rec["digest"] == kernel_digest():
         traffic = rec["fetch"] + rec["write"]
     fig = {
         "workload": f"fused o-proj + AttnRes, M={M}, K={K}, N=H={H}, nb={nb}, "
-                    f"write={write}, has_delta={has_delta}, aux=1, final={final}",
-        "M": M, "K": K, "nb": nb, "write": write,
+                    f"write={write}, has_delta={has_delta}, aux=1, final={final}, "
+                    f"W {'prepared (tile-major)' if packed else 'row-major'}",
+        "M": M, "K": K, "nb": nb, "write": write, "w_layout": "prepared" if packed else "row-major",
         "us_per_layer_step": round(us_step, 3),
         "achieved_GBs": round(gbs, 1),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1),
@@ -463,6 +470,8 @@ def main():
     ap.add_argument("--only", action="store_true",
                     help="time only --config (the default run times configs 0, 1 and 2)")
     ap.add_argument("--final", type=int, default=0)
+    ap.add_argument("--w-layout", choices=["prepared", "row-major", "both"], default="both",
+                    help="W layout of the timed steps (the headline takes the first measured)")
     ap.add_argument("--cpu-seconds", type=float, default=6.0,
                     help="bounded host time per leg of the oracle baseline (0 skips it)")
     ap.add_argument("--no-check", action="store_true")
@@ -503,10 +512,13 @@ def main():
 
     head = args.config
     order = [head] if args.only else [head] + [c for c in sorted(WORKLOADS) if c != head]
+    layouts = {"prepared": [True], "row-major": [False], "both": [True, False]}[args.w_layout]
     figs, inputs = {}, {}
     for c in order:
-        figs[c], inputs[c] = fused_measure(c, args, np, torch, sga, synth, dev, final=args.final)
-    f = figs[head]
+        for pk in layouts:
+            figs[(c, pk)], inputs[c] = fused_measure(c, args, np, torch, sga, synth, dev,
+                                                     final=args.final, packed=pk)
+    f = figs[(head, layouts[0])]
     us_step = f["us_per_layer_step"]
     gbs = f["achieved_GBs"]
 
@@ -545,7 +557,7 @@ def main():
             "traffic_note": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated); "
                             "null unless measured on these kernel sources",
         },
-        "workloads": [figs[c] for c in sorted(figs)],
+        "workloads": [figs[k] for k in sorted(figs, key=lambda k: (k[0], not k[1]))],
     }
 
     if args.stream_read_gb > 0:

@@ -231,6 +231,55 @@ int attnres_oproj_run(const void* x, int64_t ldx, const void* W, int64_t ldw, in
                       int final_boundary, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attnres_packed_weights_size - bytes of the prepared (tile-major) layout of
+ * a W [N, K] for attnres_oproj_packed_run: 256 * N * 4 * ceil(K / 512).
+ */
+size_t attnres_packed_weights_size(int N, int K);
+
+/*
+ * attnres_pack_weights - writes W [N, K] (bf16, row stride ldw) once in the
+ * prepared layout that attnres_oproj_packed_run streams (oproj.prepared page,
+ * PreparedOproj.__init__: the projection weight is bound once, when the layer
+ * is prepared, not per step). Layout: P = 4 * ceil(K / 512) planes of 128
+ * k-values; plane j holds every row's k-values [128 j, 128 j + 128) as one
+ * 256-byte segment, rows in order (segment of row n at byte (j N + n) * 256),
+ * and inside the segment of row n the 16-byte piece p (k-values 8p .. 8p + 7
+ * of the plane) sits at position p ^ (n & 15); k-values at or past K are
+ * zero. The step then reads each plane front to back in whole segments of
+ * consecutive rows, and the pieces land in LDS in the order its matrix-core
+ * reads expect.
+ *   W: device memory, 16-byte aligned, ldw >= K, a multiple of 8; K % 8 == 0;
+ *   Wp: device memory of at least attnres_packed_weights_size(N, K) bytes,
+ *   16-byte aligned, not overlapping W (written completely).
+ *   N == 0 or K == 0 returns ATTNRES_OK at once.
+ * Errors: ATTNRES_EINVAL (NULL, ldw < K, Wp too small), ATTNRES_EALIGN,
+ * ATTNRES_EUNSUPPORTED (K % 8 != 0), ATTNRES_EHIP.
+ */
+int attnres_pack_weights(const void* W, int64_t ldw, int N, int K, void* Wp, size_t Wp_bytes,
+                         void* stream);
+
+/*
+ * attnres_oproj_packed_run - attnres_oproj_run with W given in the prepared
+ * layout (attnres_pack_weights of W [H, K]; Wp_bytes at least
+ * attnres_packed_weights_size(H, K)). Up to 32 tokens it is the same
+ * arithmetic in the same order: the outputs equal attnres_oproj_run's on the
+ * row-major W bit for bit. Beyond 32 tokens, where two workgroups split K,
+ * each workgroup takes its chunks of a prepared W in K order (all of them
+ * sweep the planes together), while attnres_oproj_run starts each workgroup
+ * at a different chunk (workgroups sharing x then read different parts of it
+ * at a time): the FP32 sums then differ by rounding only.
+ * Arguments and errors as for attnres_oproj_run (ldw is not needed); a
+ * prepared W of 2^32 bytes or more returns ATTNRES_EUNSUPPORTED.
+ */
+int attnres_oproj_packed_run(const void* x, int64_t ldx, const void* Wp, size_t Wp_bytes, int K,
+                             void* prefix, int64_t ld_prefix, void* blocks, int64_t blk_stride_t,
+                             int64_t blk_stride_b, int cap, const void* norm, const void* query,
+                             const void* out_norm, void* out, int64_t ld_out, void* aux,
+                             int64_t ld_aux, float eps, float out_eps, int M, int H, int nb,
+                             int write, int has_delta, int final_boundary, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * attnres_oproj_run_noalloc - attnres_oproj_run without a caller workspace,
  * for callers that cannot allocate device memory (code under stream capture,
  * tight serving loops, harnesses that forbid allocation). It allocates

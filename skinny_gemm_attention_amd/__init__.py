@@ -43,6 +43,14 @@ _lib.attnres_oproj_workspace_init.restype = _I
 _lib.attnres_oproj_run.argtypes = [_P, _I64, _P, _I64, _I, _P, _I64, _P, _I64, _I64, _I, _P, _P,
                                    _P, _P, _I64, _P, _I64, _F, _F, _I, _I, _I, _I, _I, _I, _P,
                                    _SZ, _P]
+_lib.attnres_packed_weights_size.argtypes = [_I, _I]
+_lib.attnres_packed_weights_size.restype = _SZ
+_lib.attnres_pack_weights.argtypes = [_P, _I64, _I, _I, _P, _SZ, _P]
+_lib.attnres_pack_weights.restype = _I
+_lib.attnres_oproj_packed_run.argtypes = [_P, _I64, _P, _SZ, _I, _P, _I64, _P, _I64, _I64, _I,
+                                          _P, _P, _P, _P, _I64, _P, _I64, _F, _F, _I, _I, _I, _I,
+                                          _I, _I, _P, _SZ, _P]
+_lib.attnres_oproj_packed_run.restype = _I
 _lib.attnres_oproj_run_noalloc.argtypes = [_P, _I64, _P, _I64, _I, _P, _I64, _P, _I64, _I64, _I,
                                            _P, _P, _P, _P, _I64, _P, _I64, _F, _F, _I, _I, _I, _I,
                                            _I, _I, _P]
@@ -67,7 +75,8 @@ EXPORTS = ("attnres_run", "wsgemm_run", "wsgemm_moe_front_run", "wsgemm_workspac
            "attnres_oproj_run", "attnres_oproj_workspace_size",
            "attnres_oproj_workspace_init", "attnres_oproj_ahead_run", "attnres_post_run",
            "attnres_strerror", "attnres_stream_read", "attnres_workspace_status",
-           "attnres_oproj_run_noalloc")
+           "attnres_oproj_run_noalloc", "attnres_packed_weights_size", "attnres_pack_weights",
+           "attnres_oproj_packed_run")
 
 STREAM_READ_SINK_WORDS = 65536  # ATTNRES_STREAM_READ_SINK_WORDS
 EWAIT = -7  # ATTNRES_EWAIT: a wait of an earlier call on the workspace gave up
@@ -319,6 +328,50 @@ def attnres_oproj_run(x, W, prefix, blocks, norm, query, out_norm, out, aux, wor
                                 _ptr(aux), _row_stride(aux), eps, out_eps, M, H, nb, write,
                                 int(has_delta), int(final_boundary), ws, wsb, _stream(stream))
     _check(rc, "attnres_oproj_run")
+    return out, prefix, blocks
+
+
+def attnres_packed_weights_size(N: int, K: int) -> int:
+    return int(_lib.attnres_packed_weights_size(N, K))
+
+
+def attnres_pack_weights(W, Wp=None, stream=None):
+    """W [N, K] in the prepared (tile-major) layout of attnres_oproj_packed_run;
+    Wp (uint8 or 16-bit, at least attnres_packed_weights_size(N, K) bytes) is
+    allocated here by torch when not given. Returns Wp."""
+    N, K = W.shape
+    nbytes = attnres_packed_weights_size(N, K)
+    if Wp is None:
+        Wp = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=W.device)
+    have = Wp.numel() * Wp.element_size()
+    if have < nbytes:
+        raise AttnResError(-1, f"Wp must hold >= {nbytes} bytes, got {have}")
+    rc = _lib.attnres_pack_weights(_ptr(W), _row_stride(W), N, K,
+                                   ctypes.c_void_p(Wp.data_ptr()), have, _stream(stream))
+    _check(rc, "attnres_pack_weights")
+    return Wp
+
+
+def attnres_oproj_packed_run(x, Wp, H, prefix, blocks, norm, query, out_norm, out, aux, workspace,
+                             *, nb, write=-1, has_delta=1, final_boundary=0, eps=1e-6,
+                             out_eps=1e-6, stream=None):
+    """attnres_oproj_run with W [H, K] given as attnres_pack_weights(W)."""
+    M, K = x.shape
+    _attn_shapes(M, H, prefix, blocks, norm, query, out_norm, out, aux)
+    have = Wp.numel() * Wp.element_size()
+    if have < attnres_packed_weights_size(H, K):
+        raise AttnResError(-1, f"Wp must hold >= {attnres_packed_weights_size(H, K)} bytes")
+    if not Wp.is_cuda:
+        raise AttnResError(-1, "tensors must be on the GPU")
+    bst_t, bst_b, cap = _block_strides(blocks)
+    ws = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.attnres_oproj_packed_run(
+        _ptr(x), _row_stride(x), ctypes.c_void_p(Wp.data_ptr()), have, K, _ptr(prefix),
+        _row_stride(prefix), _ptr(blocks), bst_t, bst_b, cap, _ptr(norm), _ptr(query),
+        _ptr(out_norm), _ptr(out), _row_stride(out), _ptr(aux), _row_stride(aux), eps, out_eps, M,
+        H, nb, write, int(has_delta), int(final_boundary), ws, wsb, _stream(stream))
+    _check(rc, "attnres_oproj_packed_run")
     return out, prefix, blocks
 
 

@@ -325,7 +325,7 @@ int oproj_common(const void* x, int64_t ldx, const void* W, int64_t ldw, int K, 
                  int64_t ld_out, void* aux, int64_t ld_aux, float eps, float out_eps, int M, int H,
                  int nb, int write, int has_delta, int final_boundary, void* workspace,
                  size_t workspace_bytes, const attnres::AheadParams& ah, void* stream,
-                 bool library_ws = false) {
+                 bool library_ws = false, bool packed_w = false, size_t w_bytes = 0) {
   int rc = check_attnres(prefix, ld_prefix, blocks, blk_stride_t, blk_stride_b, cap, norm, query,
                          out_norm, out, ld_out, aux, ld_aux, eps, out_eps, M, H, nb, write,
                          has_delta, final_boundary);
@@ -333,9 +333,12 @@ int oproj_common(const void* x, int64_t ldx, const void* W, int64_t ldw, int K, 
   if (K < 0 || (K > 0 && (!x || !W))) return ATTNRES_EINVAL;  // x, W unread when K == 0
   if (M < 1 || M > ATTNRES_MAX_M) return ATTNRES_ERANGE;
   if (K & 7) return ATTNRES_EUNSUPPORTED;
-  if (K > 0 && (ldx < K || ldw < K)) return ATTNRES_EINVAL;
+  if (K > 0 && (ldx < K || (!packed_w && ldw < K))) return ATTNRES_EINVAL;
+  if (K > 0 && packed_w && w_bytes < attnres::packed_bytes(H, K)) return ATTNRES_EINVAL;
+  if (K > 0 && packed_w && attnres::packed_bytes(H, K) >= ((size_t)1 << 32))
+    return ATTNRES_EUNSUPPORTED;  // prepared W is addressed with 32-bit offsets
   if (K > 0 && (!aligned16(x) || !aligned16(W))) return ATTNRES_EALIGN;
-  if (K > 0 && (!stride8(ldx) || !stride8(ldw))) return ATTNRES_EALIGN;
+  if (K > 0 && (!stride8(ldx) || (!packed_w && !stride8(ldw)))) return ATTNRES_EALIGN;
   if (library_ws) {
     // never reached within the limits above: the array covers 64 tokens of
     // the widest rows
@@ -361,6 +364,7 @@ int oproj_common(const void* x, int64_t ldx, const void* W, int64_t ldw, int K, 
   p.partials = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
                                            attnres::kWorkspaceHeader + mailbox_bytes(M, H));
   p.ng = 0;
+  p.wrows = packed_w ? H : 0;
   p.ah = ah;
   return from_hip(attnres::launch_fused(p, static_cast<hipStream_t>(stream)));
 }
@@ -381,6 +385,38 @@ int attnres_oproj_run(const void* x, int64_t ldx, const void* W, int64_t ldw, in
                       cap, norm, query, out_norm, out, ld_out, aux, ld_aux, eps, out_eps, M, H,
                       nb, write, has_delta, final_boundary, workspace, workspace_bytes, ah,
                       stream);
+}
+
+size_t attnres_packed_weights_size(int N, int K) {
+  if (N < 0 || K < 0) return 0;
+  return attnres::packed_bytes(N, K);
+}
+
+int attnres_pack_weights(const void* W, int64_t ldw, int N, int K, void* Wp, size_t Wp_bytes,
+                         void* stream) {
+  if (N < 0 || K < 0) return ATTNRES_EINVAL;
+  if (N == 0 || K == 0) return ATTNRES_OK;  // nothing to read or write
+  if (!W || !Wp || ldw < K) return ATTNRES_EINVAL;
+  if ((K & 7) || N > (1 << 24)) return ATTNRES_EUNSUPPORTED;
+  if (!aligned16(W) || !aligned16(Wp) || !stride8(ldw)) return ATTNRES_EALIGN;
+  if (Wp_bytes < attnres::packed_bytes(N, K)) return ATTNRES_EINVAL;
+  return from_hip(attnres::launch_pack_weights(static_cast<const uint16_t*>(W), ldw, N, K,
+                                               static_cast<uint16_t*>(Wp),
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int attnres_oproj_packed_run(const void* x, int64_t ldx, const void* Wp, size_t Wp_bytes, int K,
+                             void* prefix, int64_t ld_prefix, void* blocks, int64_t blk_stride_t,
+                             int64_t blk_stride_b, int cap, const void* norm, const void* query,
+                             const void* out_norm, void* out, int64_t ld_out, void* aux,
+                             int64_t ld_aux, float eps, float out_eps, int M, int H, int nb,
+                             int write, int has_delta, int final_boundary, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  attnres::AheadParams ah = {nullptr, nullptr, 0.0f, nullptr, 0, nullptr};
+  return oproj_common(x, ldx, Wp, 0, K, prefix, ld_prefix, blocks, blk_stride_t, blk_stride_b,
+                      cap, norm, query, out_norm, out, ld_out, aux, ld_aux, eps, out_eps, M, H,
+                      nb, write, has_delta, final_boundary, workspace, workspace_bytes, ah, stream,
+                      false, true, Wp_bytes);
 }
 
 int attnres_oproj_run_noalloc(const void* x, int64_t ldx, const void* W, int64_t ldw, int K,

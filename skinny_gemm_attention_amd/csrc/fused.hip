@@ -68,20 +68,20 @@ __device__ __forceinline__ void load_mix(const float* row, int c, bool valid, fl
   }
 }
 
-template <bool SPLIT, int RT, int TT>
+template <bool SPLIT, int RT, int TT, bool PACKED>
 struct FusedCore {
-  using type = GemmLdsFor<RT, TT>;
+  using type = GemmLdsFor<RT, TT, PACKED>;
 };
-template <int RT, int TT>
-struct FusedCore<true, RT, TT> {
+template <int RT, int TT, bool PACKED>
+struct FusedCore<true, RT, TT, PACKED> {
   static_assert(RT * 16 == kSplitRows, "split-K row groups");
-  using type = GemmLdsSplit<TT>;
+  using type = GemmLdsSplit<TT, PACKED>;
 };
 
-template <int RT, int TT, bool SPLIT, bool AHEAD>
+template <int RT, int TT, bool SPLIT, bool AHEAD, bool PACKED>
 __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, int NO) {
   constexpr int NT = kTokenThreads, NW = NT / 64;
-  using C = typename FusedCore<SPLIT, RT, TT>::type;
+  using C = typename FusedCore<SPLIT, RT, TT, PACKED>::type;
   static_assert(C::NT == NT, "one workgroup shape for both roles");
   // tokens per owner: one up to 32 tokens, two beyond
   constexpr int KT = TT <= 2 ? 1 : kMaxTokensPerOwner;
@@ -152,8 +152,10 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
     }
     {
       C core;
-      core.start(f.x, f.ldx, f.W, f.ldw, M, kbeg, klen, row0, rows, sm.ring, SPLIT ? rg : 0,
-                 SPLIT ? 2 : 1, SPLIT ? kSplitBlock : 1);
+      // (a prepared W is swept plane by plane by all workgroups together, so
+      // its chunks are not rotated)
+      core.start(f.x, f.ldx, f.W, f.ldw, M, kbeg, klen, row0, rows, sm.ring, SPLIT && !PACKED ? rg : 0,
+                 SPLIT ? 2 : 1, SPLIT ? kSplitBlock : 1, PACKED ? f.wrows : 0);
       core.finish();
       core.stash(red);
     }
@@ -508,18 +510,25 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
   }
 }
 
-// Two kernel templates over one body (rather than one kernel template with a
-// look-ahead flag): hipcc emitted the host launch stub of only one of two
-// kernel instantiations that differed in nothing but such a flag.
+// Three kernel templates over one body (rather than one kernel template with
+// look-ahead and W-layout flags): hipcc emitted the host launch stub of only
+// one of two kernel instantiations that differed in nothing but such a flag.
 template <int RT, int TT, bool SPLIT>
 __global__ __launch_bounds__(kTokenThreads) void fused_kernel(FusedParams f, int R, int G, int NO) {
-  fused_body<RT, TT, SPLIT, false>(f, R, G, NO);
+  fused_body<RT, TT, SPLIT, false, false>(f, R, G, NO);
 }
 
 template <int RT, int TT, bool SPLIT>
 __global__ __launch_bounds__(kTokenThreads) void fused_ahead_kernel(FusedParams f, int R, int G,
                                                                      int NO) {
-  fused_body<RT, TT, SPLIT, true>(f, R, G, NO);
+  fused_body<RT, TT, SPLIT, true, false>(f, R, G, NO);
+}
+
+// W in the prepared layout (attnres_oproj_packed_run; no look-ahead variant)
+template <int RT, int TT, bool SPLIT>
+__global__ __launch_bounds__(kTokenThreads) void fused_packed_kernel(FusedParams f, int R, int G,
+                                                                      int NO) {
+  fused_body<RT, TT, SPLIT, false, true>(f, R, G, NO);
 }
 
 __global__ void workspace_init_kernel(unsigned* ws, size_t words) {
@@ -555,7 +564,10 @@ namespace {
 
 template <int RT, int TT, bool SPLIT = false>
 hipError_t go(const FusedParams& p, int R, int G, int NO, hipStream_t stream) {
-  if (p.ah.mix)
+  if (p.wrows > 0)
+    hipLaunchKernelGGL((fused_packed_kernel<RT, TT, SPLIT>), dim3(G + NO), dim3(kTokenThreads), 0,
+                       stream, p, R, G, NO);
+  else if (p.ah.mix)
     hipLaunchKernelGGL((fused_ahead_kernel<RT, TT, SPLIT>), dim3(G + NO), dim3(kTokenThreads), 0,
                        stream, p, R, G, NO);
   else

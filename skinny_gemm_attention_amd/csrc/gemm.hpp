@@ -42,9 +42,16 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 //     blocks of cblock consecutive chunks, every cstride-th block, so two
 //     workgroups can split K by taking alternate blocks (the caller adds
 //     their partial products). cstride = cblock = 1 streams the whole range.
-//   * Inside a row the 16-byte pieces are stored XOR-swizzled by (row & 15):
-//     piece p of LDS row r sits at position p ^ (r & 15). An MFMA fragment
-//     read (16 rows, one piece each) then touches 16 distinct bank groups.
+//   * Inside a row the 16-byte pieces are stored XOR-swizzled: piece p of a
+//     row sits at position p ^ key, with key = (LDS row) & 15, or for the W
+//     rows of a prepared W (global row) & 15. An MFMA fragment read (16
+//     consecutive rows, one piece each) then touches 16 distinct bank groups.
+//   * W is read either row-major (row n at W + n ldw) or from the tile-major
+//     prepared layout (pack_kernel): planes of 128 k-values of every row,
+//     each row's 256-byte segment already swizzled by its global row & 15, so
+//     a load instruction reads whole contiguous 256-byte segments of
+//     consecutive rows and lands in LDS in the order the reads expect; the
+//     workgroups of a launch together sweep each plane front to back.
 //   * Rows past R, tokens past M and pieces past K are never loaded. Stale LDS
 //     in rows past R or tokens past M only reaches output rows / tokens that
 //     are discarded (MFMA output elements are independent); k-steps that
@@ -58,7 +65,7 @@ constexpr int kCacheNT = 2;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-template <int RT, int TT, int KCB, int NSLOT>
+template <int RT, int TT, int KCB, int NSLOT, bool PACKED = false>
 struct GemmLds {
   static constexpr int NW = 8, NT = NW * 64;
   static constexpr int kQuads = RT * TT * 64;
@@ -84,7 +91,8 @@ struct GemmLds {
   uint32_t dst[MAXSEG];     // segment offset inside a slot (wave-uniform)
   uint32_t kb[MAXSEG];      // byte offset of this lane's piece inside a chunk
   bool rv[MAXSEG];          // this lane's row exists
-  int nseg, nwseg, nC, rot, K, cs, cbk, wave, kp, rh, r16, kq;
+  uint32_t wstep;           // prepared W: bytes from one chunk of a row to the next
+  int nseg, nwseg, nC, rot, K, cs, cbk, wave, kp, rh, r16, kq, akey;
   f32x4 acc[RTW][TT];
 
   // Chunks are consumed in the order rot, rot + 1, ..., wrapping around.
@@ -97,7 +105,9 @@ struct GemmLds {
   __device__ __forceinline__ int coff(int p) const { return (p / cbk) * cbk * cs + p % cbk; }
 
   __device__ __forceinline__ void issue(int c) {
-    const uint32_t cb = (uint32_t)coff(phys(c)) * KCB;
+    const uint32_t ci = (uint32_t)coff(phys(c));
+    const uint32_t cb = ci * KCB;                  // x (and row-major W): bytes into the row
+    const uint32_t cw = PACKED ? ci * wstep : cb;  // W: bytes to this chunk
     lds_char* slot = ring + (c % NSLOT) * SLOT;
     if (KCB < 1024 && cb + KCB <= (uint32_t)(2 * K)) {
       // a whole chunk: every lane loads (lanes of rows past R or M read row
@@ -106,18 +116,20 @@ struct GemmLds {
 #pragma unroll
       for (int i = 0; i < MAXSEG; ++i) {
         if (i < nwseg)  // W is read once: non-temporal
-          __builtin_amdgcn_global_load_lds(gp[i] + cb, slot + dst[i], 16, 0, kCacheNT);
+          __builtin_amdgcn_global_load_lds(gp[i] + cw, slot + dst[i], 16, 0, kCacheNT);
         else if (i < nseg)
           __builtin_amdgcn_global_load_lds(gp[i] + cb, slot + dst[i], 16, 0, 0);
       }
       return;
     }
+    // a chunk that K cuts: lanes past K skip their load (a prepared W is
+    // zero-padded, so all its lanes load: kb = 0)
 #pragma unroll
     for (int i = 0; i < MAXSEG; ++i) {
       if (i < nseg) {
         if (rv[i] && cb + kb[i] < (uint32_t)(2 * K)) {
           if (i < nwseg)  // W is read once: non-temporal
-            __builtin_amdgcn_global_load_lds(gp[i] + cb, slot + dst[i], 16, 0, kCacheNT);
+            __builtin_amdgcn_global_load_lds(gp[i] + cw, slot + dst[i], 16, 0, kCacheNT);
           else
             __builtin_amdgcn_global_load_lds(gp[i] + cb, slot + dst[i], 16, 0, 0);
         }
@@ -130,11 +142,14 @@ struct GemmLds {
   // of rows [row0, row0 + rows) (blocks of cblock chunks, every cstride-th
   // block) and issues the first NSLOT - 1 chunks. With rot_ > 0 the chunks
   // are taken in rotated order (workgroups that share x then read different
-  // parts of it at a time); the order is fixed per call.
+  // parts of it at a time); the order is fixed per call. W is row-major with
+  // row stride ldw, or with PACKED the prepared layout of a matrix of wrows
+  // rows (ldw unused; k_begin a multiple of 128; fewer than 2^32 bytes).
   __device__ __forceinline__ void start(const uint16_t* __restrict__ x, int64_t ldx,
                                         const uint16_t* __restrict__ W, int64_t ldw, int M,
                                         int k_begin, int K_, int row0, int rows, char* lds,
-                                        int rot_ = 0, int cstride = 1, int cblock = 1) {
+                                        int rot_ = 0, int cstride = 1, int cblock = 1,
+                                        int wrows = 0) {
     const int lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     kp = wave % NP;
@@ -156,18 +171,31 @@ struct GemmLds {
     nseg = wave < S ? (S - wave + NW - 1) / NW : 0;
     nwseg = wave < wseg ? (wseg - wave + NW - 1) / NW : 0;  // W segments come first
     const int lr = lane / PIECES, q = lane % PIECES;
+    // swizzle key of the W rows this lane reads as A: the global row for a
+    // prepared W (swizzled when it was prepared), else the LDS row
+    if (PACKED) {
+      akey = (row0 + r16) & 15;
+      wstep = (uint32_t)(KCB / 256) * (uint32_t)wrows * 256u;
+    }
 #pragma unroll
     for (int i = 0; i < MAXSEG; ++i) {
       const int sidx = wave + i * NW;
       const bool isw = sidx < wseg;
       const int r = (isw ? sidx : sidx - wseg) * RPI + lr;  // row within W rows or x rows
-      const int lrow = (isw ? 0 : WROWS) + r;                // LDS row
-      const int p = q ^ (lrow & 15);
       rv[i] = isw ? r < rows : r < M;
       const int rr = rv[i] ? r : 0;
-      gp[i] = isw ? reinterpret_cast<const char*>(W + (size_t)(row0 + rr) * ldw + k_begin) + 16 * p
-                  : reinterpret_cast<const char*>(x + (size_t)rr * ldx + k_begin) + 16 * p;
-      kb[i] = 16 * p;
+      if (PACKED && isw) {
+        // prepared W: position q of this row's chunk is position q % 16 of
+        // its segment in plane k_begin / 128 + q / 16 (already swizzled)
+        gp[i] = reinterpret_cast<const char*>(W) +
+                ((size_t)(k_begin / 128 + q / 16) * wrows + (size_t)(row0 + rr)) * 256 + 16 * (q % 16);
+        kb[i] = 0;
+      } else {
+        const int p = q ^ (r & 15);  // LDS row & 15 (W rows start at LDS row 0, x rows at WROWS)
+        gp[i] = isw ? reinterpret_cast<const char*>(W + (size_t)(row0 + rr) * ldw + k_begin) + 16 * p
+                    : reinterpret_cast<const char*>(x + (size_t)rr * ldx + k_begin) + 16 * p;
+        kb[i] = 16 * p;
+      }
       dst[i] = __builtin_amdgcn_readfirstlane(((isw ? 0 : WROWS) + (sidx < wseg ? sidx : sidx - wseg) * RPI) * KCB);
     }
 #pragma unroll
@@ -177,6 +205,69 @@ struct GemmLds {
     for (int c = 0; c < NSLOT - 1 && c < nC; ++c) issue(c);
   }
 
+  // One chunk's operands for this wavefront: the A (W rows) and B (x rows)
+  // fragments of its k-steps. live: the k-step starts inside K (wave-uniform);
+  // cut: this lane's 8 k-values lie past K, so its operands count as zero.
+  struct Frags {
+    u32x4 a[SPW][RTW], b[SPW][TT];
+    bool live[SPW], cut[SPW];
+  };
+
+  // Issues the LDS reads of chunk c's fragments; nothing waits for them here.
+  __device__ __forceinline__ void load_frags(int c, Frags& f) const {
+    const lds_char* slot = ring + (c % NSLOT) * SLOT;
+    const int cbase = coff(phys(c)) * KE;
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int ks = kp * SPW + j;
+      const int k0 = cbase + ks * 32;
+      f.live[j] = k0 < K;
+      f.cut[j] = k0 + 8 * kq >= K;
+      if (f.live[j]) {
+        const int offb = 16 * ((ks * 4 + kq) ^ r16);
+        const int offa = PACKED ? 16 * ((ks * 4 + kq) ^ akey) : offb;
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+          f.a[j][rt] = *reinterpret_cast<const lds_u32x4*>(slot + ((rh * RTW + rt) * 16 + r16) * KCB + offa);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+          f.b[j][tt] = *reinterpret_cast<const lds_u32x4*>(slot + (WROWS + tt * 16 + r16) * KCB + offb);
+      }
+    }
+  }
+
+  // The matrix-core products of one chunk's fragments, in k-step order.
+  __device__ __forceinline__ void mma(Frags& f) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      if (f.live[j]) {
+        if (f.cut[j]) {
+#pragma unroll
+          for (int rt = 0; rt < RTW; ++rt) f.a[j][rt] = zero;
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) f.b[j][tt] = zero;
+        }
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) acc[rt][tt] = mfma_bf16(f.a[j][rt], f.b[j][tt], acc[rt][tt]);
+      }
+    }
+  }
+
+  // Waits until chunk c is in LDS for every wavefront (and every wavefront has
+  // finished reading chunk c - 1, whose slot is refilled here), issues chunk
+  // c + NSLOT - 1 and the LDS reads of chunk c's fragments.
+  __device__ __forceinline__ void step(int c, Frags& f) {
+    const int ahead = min(c + NSLOT - 2, nC - 1) - c;  // chunks after c already issued
+    wait_vmem_upto<MAXSEG * (NSLOT - 2)>(nseg * ahead);  // also lgkmcnt(0): earlier fragment reads
+    wg_barrier();
+    if (c + NSLOT - 1 < nC) issue(c + NSLOT - 1);
+    load_frags(c, f);
+  }
+
+  // Reads chunk c's fragments and runs their products at once (wide tiles).
   __device__ __forceinline__ void compute(int c) {
     const lds_char* slot = ring + (c % NSLOT) * SLOT;
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -185,14 +276,15 @@ struct GemmLds {
       const int ks = kp * SPW + j;
       const int k0 = coff(phys(c)) * KE + ks * 32;
       if (k0 < K) {
-        const int off = 16 * ((ks * 4 + kq) ^ r16);
+        const int offb = 16 * ((ks * 4 + kq) ^ r16);
+        const int offa = PACKED ? 16 * ((ks * 4 + kq) ^ akey) : offb;
         u32x4 a[RTW], b[TT];
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
-          a[rt] = *reinterpret_cast<const lds_u32x4*>(slot + ((rh * RTW + rt) * 16 + r16) * KCB + off);
+          a[rt] = *reinterpret_cast<const lds_u32x4*>(slot + ((rh * RTW + rt) * 16 + r16) * KCB + offa);
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
-          b[tt] = *reinterpret_cast<const lds_u32x4*>(slot + (WROWS + tt * 16 + r16) * KCB + off);
+          b[tt] = *reinterpret_cast<const lds_u32x4*>(slot + (WROWS + tt * 16 + r16) * KCB + offb);
         if (k0 + 32 > K && k0 + 8 * kq >= K) {
 #pragma unroll
           for (int rt = 0; rt < RTW; ++rt) a[rt] = zero;
@@ -208,14 +300,39 @@ struct GemmLds {
   }
 
   // Consumes every chunk; returns with all loads complete and all wavefronts
-  // past their last LDS read of the ring.
+  // past their last LDS read of the ring. Up to two token tiles the loop is
+  // software-pipelined by one chunk: the products of chunk c - 1 run while
+  // chunk c's fragment reads are in flight (two fragment sets in turn; the
+  // products keep chunk order). Wider tiles (twice the fragment registers)
+  // read and multiply each chunk in turn: written as load_frags + mma, that
+  // loop made the compiler wait for the chunk's own LDS traffic before its
+  // fragment reads (64 tokens, K = 8192: 31.0 -> 36.8 us).
   __device__ __forceinline__ void finish() {
-    for (int c = 0; c < nC; ++c) {
-      const int ahead = min(c + NSLOT - 2, nC - 1) - c;  // chunks after c already issued
-      wait_vmem_upto<MAXSEG * (NSLOT - 2)>(nseg * ahead);
-      wg_barrier();
-      if (c + NSLOT - 1 < nC) issue(c + NSLOT - 1);
-      compute(c);
+    if (TT > 2) {
+      for (int c = 0; c < nC; ++c) {
+        const int ahead = min(c + NSLOT - 2, nC - 1) - c;  // chunks after c already issued
+        wait_vmem_upto<MAXSEG * (NSLOT - 2)>(nseg * ahead);
+        wg_barrier();
+        if (c + NSLOT - 1 < nC) issue(c + NSLOT - 1);
+        compute(c);
+      }
+    } else if (nC > 0) {
+      Frags f0, f1;
+      step(0, f0);
+      int c = 1;
+      for (; c + 1 < nC; c += 2) {
+        step(c, f1);
+        mma(f0);
+        step(c + 1, f0);
+        mma(f1);
+      }
+      if (c < nC) {
+        step(c, f1);
+        mma(f0);
+        mma(f1);
+      } else {
+        mma(f0);
+      }
     }
     wait_vmem_n<0>();
     wg_barrier();
@@ -257,16 +374,16 @@ struct GemmLds {
 // slots (128 KB) for a single row tile (wsgemm_run at M <= 16, N = 4096: 5%
 // faster than three slots; five do not fit beside the fused kernel's other
 // LDS); 512-byte segments beyond 16 tokens, where x dominates a chunk.
-template <int RT, int TT>
+template <int RT, int TT, bool PACKED = false>
 using GemmLdsFor = GemmLds<RT, TT, (TT == 1 && RT == 1 ? 1024 : 512),
-                           (TT == 1 ? 4 : TT == 2 ? 4 : 3)>;
+                           (TT == 1 ? 4 : TT == 2 ? 4 : 3), PACKED>;
 
 // Split-K tiles for more than 32 tokens: 64 rows (four row tiles) per
 // workgroup over half of K, 256-byte row segments in four slots; wavefronts
 // split into four k-steps by two row groups.
 constexpr int kSplitRows = 64;
-template <int TT>
-using GemmLdsSplit = GemmLds<4, TT, 256, (TT <= 4 ? 4 : 3)>;  // three slots beyond 64 tokens
+template <int TT, bool PACKED = false>
+using GemmLdsSplit = GemmLds<4, TT, 256, (TT <= 4 ? 4 : 3), PACKED>;  // three slots beyond 64 tokens
 
 // Rows of W per workgroup for N output rows: spread N over 256 workgroups (one
 // per compute unit), a multiple of 4, at most 32 (two 16-row MFMA tiles).

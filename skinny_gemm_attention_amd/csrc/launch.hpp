@@ -74,8 +74,17 @@ struct FusedParams {
   unsigned* mailbox;   // [M][H / 2]
   unsigned* partials;  // split-K hand-off (see above)
   int ng;              // split-K row groups (0: no split)
+  int wrows;           // 0: W row-major (row stride ldw); else W prepared (pack_kernel) with wrows rows
   AheadParams ah;      // ah.mix == nullptr: no look-ahead statistics
 };
+
+// The prepared (tile-major) layout of a W [N, K] bf16 (pack_kernel):
+// P = 4 ceil(K / 512) planes of 128 k-values; plane j holds every row's
+// k-values [128 j, 128 j + 128) as one 256-byte segment, rows in order, and
+// within the segment of row n the 16-byte piece p (k-values 8p .. 8p + 7) sits
+// at position p ^ (n & 15); k-values at or past K are zero.
+inline size_t packed_planes(int K) { return 4 * (((size_t)K + 511) / 512); }
+inline size_t packed_bytes(int N, int K) { return packed_planes(K) * (size_t)N * 256; }
 
 int compute_units();
 hipError_t launch_wsgemm(const GemmParams& p, hipStream_t stream);
@@ -89,5 +98,7 @@ bool wsgemm_ws_splits(int M, int N, int K, int compute_units);
 hipError_t launch_attnres(const AttnParams& p, hipStream_t stream);
 hipError_t launch_fused(const FusedParams& p, hipStream_t stream);
 hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t stream);
+hipError_t launch_pack_weights(const uint16_t* W, int64_t ldw, int N, int K, uint16_t* Wp,
+                               hipStream_t stream);
 
 }  // namespace attnres

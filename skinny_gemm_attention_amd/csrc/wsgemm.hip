@@ -197,6 +197,36 @@ __global__ __launch_bounds__(512) void wsgemm_split_kernel(GemmParams p, unsigne
   }
 }
 
+// The prepared layout of W (see packed_bytes in launch.hpp): thread i writes
+// the 16-byte piece at position j = i % 16 of row n = (i / 16) % N in plane
+// i / (16 N), which holds piece j ^ (n & 15) of that row's plane, or zeros
+// past K (K is a multiple of 8, so a piece is all in or all out).
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ W, int64_t ldw,
+                                                   int N, int K, uint16_t* __restrict__ Wp,
+                                                   size_t pieces) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < pieces;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const int j = (int)(i & 15);
+    const size_t rn = i >> 4;
+    const int n = (int)(rn % (size_t)N);
+    const size_t plane = rn / (size_t)N;
+    const size_t k = plane * 128 + (size_t)(8 * (j ^ (n & 15)));
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (k < (size_t)K) v = ld16(W + (size_t)n * ldw + k);
+    *reinterpret_cast<u32x4*>(Wp + (plane * N + n) * 128 + 8 * j) = v;
+  }
+}
+
+hipError_t launch_pack_weights(const uint16_t* W, int64_t ldw, int N, int K, uint16_t* Wp,
+                               hipStream_t stream) {
+  const size_t pieces = packed_bytes(N, K) / 16;
+  size_t blocks = (pieces + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W, ldw, N, K, Wp,
+                     pieces);
+  return hipGetLastError();
+}
+
 template <int RT, int TT>
 static hipError_t go(const GemmParams& p, int R, hipStream_t stream) {
   const int grid = (p.N + R - 1) / R;

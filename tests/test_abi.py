@@ -40,6 +40,11 @@ def lib():
                                    P, F, F, I, I, I, I, I, I, P]
     L.attnres_oproj_run_noalloc.argtypes = [P, I64, P, I64, I, P, I64, P, I64, I64, I, P, P, P,
                                             P, I64, P, I64, F, F, I, I, I, I, I, I, P]
+    L.attnres_packed_weights_size.argtypes = [I, I]
+    L.attnres_packed_weights_size.restype = SZ
+    L.attnres_pack_weights.argtypes = [P, I64, I, I, P, SZ, P]
+    L.attnres_oproj_packed_run.argtypes = [P, I64, P, SZ, I, P, I64, P, I64, I64, I, P, P, P, P,
+                                           I64, P, I64, F, F, I, I, I, I, I, I, P, SZ, P]
     L.attnres_workspace_status.argtypes = [P, SZ, P]
     L.attnres_workspace_status.restype = I
     L.attnres_stream_read.argtypes = [P, SZ, P, P]
@@ -62,7 +67,8 @@ def test_header_symbols_exported(lib):
                           "attnres_oproj_workspace_init", "attnres_oproj_run",
                           "attnres_oproj_ahead_run", "attnres_post_run", "attnres_strerror",
                           "attnres_stream_read", "attnres_workspace_status",
-                          "attnres_oproj_run_noalloc"}
+                          "attnres_oproj_run_noalloc", "attnres_packed_weights_size",
+                          "attnres_pack_weights", "attnres_oproj_packed_run"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -343,3 +349,46 @@ def test_error_codes_match_header():
     text = open(HEADER).read()
     codes = dict((n, int(v)) for n, v in re.findall(r"#define ATTNRES_(E\w+) \((-\d+)\)", text))
     assert codes["EWAIT"] == sga.EWAIT == -7
+
+
+def test_packed_weights_size(lib):
+    """4 ceil(K / 512) planes of 256-byte segments, one per row."""
+    assert lib.attnres_packed_weights_size(7168, 4096) == 7168 * 4096 * 2
+    assert lib.attnres_packed_weights_size(7168, 1000) == 7168 * 256 * 8
+    assert lib.attnres_packed_weights_size(16, 8) == 16 * 256 * 4
+    assert lib.attnres_packed_weights_size(16, 0) == 0
+
+
+def test_pack_weights_host_checks(lib):
+    """Every rejection happens on the host (no case here reaches a launch:
+    the pointers are never dereferenced)."""
+    fake = 1 << 40
+    W, Wp = ctypes.c_void_p(fake), ctypes.c_void_p(fake + (1 << 30))
+    big = 1 << 30
+    assert lib.attnres_pack_weights(None, 4096, 8, 4096, Wp, big, None) == -1
+    assert lib.attnres_pack_weights(W, 4000, 8, 4096, Wp, big, None) == -1          # ldw < K
+    assert lib.attnres_pack_weights(W, 4096, 8, 4092, Wp, big, None) == -4          # K % 8
+    assert lib.attnres_pack_weights(ctypes.c_void_p(fake + 8), 4096, 8, 4096, Wp, big, None) == -2
+    assert lib.attnres_pack_weights(W, 4100, 8, 4096, Wp, big, None) == -2          # ldw % 8
+    assert lib.attnres_pack_weights(W, 4096, 8, 4096, Wp, 8 * 4096 * 2 - 16, None) == -1
+    assert lib.attnres_pack_weights(W, 4096, 0, 4096, Wp, 0, None) == 0            # nothing to do
+
+
+def call_packed(lib, **kw):
+    a = attn_args()
+    a.update(x=A, ldx=8192, Wp=A, wpb=7168 * 8192 * 2, K=8192, ws=A, wsb=256 + 4 * 7168 * 2, M=4)
+    a.update(kw)
+    return lib.attnres_oproj_packed_run(
+        a["x"], a["ldx"], a["Wp"], a["wpb"], a["K"], a["prefix"], a["ld_prefix"], a["blocks"],
+        a["bst_t"], a["bst_b"], a["cap"], a["norm"], a["query"], a["out_norm"], a["out"],
+        a["ld_out"], a["aux"], a["ld_aux"], a["eps"], a["out_eps"], a["M"], a["H"], a["nb"],
+        a["write"], a["has_delta"], a["final"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(x=None), -1), (dict(Wp=None), -1), (dict(M=0), -3), (dict(M=65), -3),
+    (dict(K=8190), -4), (dict(ldx=4096), -1), (dict(Wp=A + 8), -2), (dict(ws=None), -5),
+    (dict(wpb=7168 * 8192 * 2 - 256), -1), (dict(H=100), -4),
+])
+def test_attnres_oproj_packed_run_rejects(lib, change, code):
+    assert call_packed(lib, **change) == code

@@ -54,8 +54,8 @@ def test_digest_ignores_comments_and_spacing():
 
 
 def test_stored_traffic_records_are_well_formed():
-    for cfg, rec in bench.MEASURED_TRAFFIC.items():
-        assert cfg in bench.WORKLOADS
+    for (cfg, layout), rec in bench.MEASURED_TRAFFIC.items():
+        assert cfg in bench.WORKLOADS and layout in ("prepared", "row-major")
         assert len(rec["digest"]) == 64 and rec["fetch"] > 0 and rec["write"] > 0
         w = bench.WORKLOADS[cfg]
         alg = bench.algorithmic_bytes(w["M"], w["K"], w["nb"], w["write"], w["has_delta"])

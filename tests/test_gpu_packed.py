@@ -1,0 +1,123 @@
+"""The prepared (tile-major) W layout and the fused step on it, HIP gfx950.
+
+attnres_pack_weights writes W [N, K] as 4 ceil(K / 512) planes of 128
+k-values: plane j holds every row's k-values [128 j, 128 j + 128) as one
+256-byte segment, rows in order, with the 16-byte piece p of row n at
+position p ^ (n & 15) and zeros past K (the weight is prepared once, as
+PreparedOproj binds it on the oproj.prepared page). The layout is checked
+element by element against that definition written out in numpy; the fused
+step on the prepared W must give attnres_oproj_run's bits on the row-major W
+(the same operands reach the same matrix-core instructions in the same
+order; up to 32 tokens, since beyond that the row-major call rotates the K
+order of each workgroup and the prepared one does not) and the oracle's
+values at the fused-step bar.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_tools import DEV, down, lib, up
+from parity_tools import check_fused_step
+
+pytestmark = pytest.mark.gpu
+POISON = 0x7FC1
+
+
+def packed_reference(W, K):
+    """The documented layout, element by element (numpy)."""
+    N = W.shape[0]
+    P = 4 * ((K + 511) // 512)
+    Wz = np.zeros((N, P * 128), np.uint16)
+    Wz[:, :K] = W[:, :K]
+    out = np.zeros((P, N, 16, 8), np.uint16)
+    for n in range(N):
+        for j in range(16):
+            p = j ^ (n & 15)
+            out[:, n, j, :] = Wz[n].reshape(P, 16, 8)[:, p, :]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("N,K,pad", [(40, 1000, 24), (16, 8, 0), (7168, 4096, 0), (33, 520, 8)])
+def test_pack_layout(N, K, pad):
+    sga = lib()
+    W = synth.normal_bf16(5, 2, N + K, (N, K))
+    Wg = torch.full((N, K + pad), POISON, dtype=torch.int16, device=DEV)
+    Wg[:, :K] = up(W)
+    nbytes = sga.attnres_packed_weights_size(N, K)
+    Wp = torch.full((nbytes // 2 + 64,), POISON, dtype=torch.int16, device=DEV)
+    sga.attnres_pack_weights(Wg[:, :K], Wp)
+    torch.cuda.synchronize()
+    got = down(Wp)
+    assert np.array_equal(got[:nbytes // 2], packed_reference(W, K)), "packed layout"
+    assert np.all(got[nbytes // 2:] == POISON), "wrote past the packed size"
+
+
+def _run(s, *, packed, final, write=None, has_delta=None):
+    sga = lib()
+    write = s.write if write is None else write
+    has_delta = s.has_delta if has_delta is None else has_delta
+    prefix, blocks = up(s.prefix), up(s.blocks)
+    out = torch.full((s.M, s.H), POISON, dtype=torch.int16, device=DEV)
+    aux = torch.full((s.M, s.H), POISON, dtype=torch.int16, device=DEV)
+    ws = sga.make_workspace(s.M, s.H, s.nb, DEV)
+    kw = dict(nb=s.nb, write=write, has_delta=has_delta, final_boundary=final, eps=s.eps,
+              out_eps=s.out_eps)
+    Wg = up(s.W)
+    if packed:
+        Wp = sga.attnres_pack_weights(Wg)
+        sga.attnres_oproj_packed_run(up(s.x), Wp, s.H, prefix, blocks, up(s.norm), up(s.query),
+                                     up(s.out_norm), out, aux, ws, **kw)
+    else:
+        sga.attnres_oproj_run(up(s.x), Wg, prefix, blocks, up(s.norm), up(s.query),
+                              up(s.out_norm), out, aux, ws, **kw)
+    assert sga.attnres_workspace_status(ws) == 0
+    torch.cuda.synchronize()
+    return {k: down(v) for k, v in (("out", out), ("prefix", prefix), ("blocks", blocks),
+                                    ("aux", aux))}
+
+
+@pytest.fixture(scope="module")
+def configs():
+    return {c: synth.config_inputs(c) for c in (0, 1, 2)}
+
+
+@pytest.mark.parametrize("final", [0, 1])
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+def test_packed_equals_row_major_and_oracle(configs, cfg, final):
+    s = configs[cfg]
+    a = _run(s, packed=True, final=final)
+    if s.M <= 32:
+        b = _run(s, packed=False, final=final)
+        for k in ("out", "prefix", "blocks", "aux"):
+            assert np.array_equal(a[k], b[k]), f"cfg{cfg} final={final}: {k} differs"
+    assert np.array_equal(a["aux"], a["prefix"])
+    if s.write >= 0:
+        assert np.array_equal(a["blocks"][:, s.write], a["prefix"])
+    check_fused_step(x=s.x, W=s.W, old_prefix=s.prefix, blocks=s.blocks, norm=s.norm,
+                     query=s.query, out_norm=s.out_norm, nb=s.nb, write=s.write,
+                     has_delta=s.has_delta, final=final, eps=s.eps, out_eps=s.out_eps,
+                     gpu_out=a["out"], gpu_new=a["prefix"], what=f"packed cfg{cfg}")
+
+
+@pytest.mark.parametrize("M,K,H,nb,cap,write,has_delta", [
+    (13, 1000, 1024, 3, 4, 3, 1),   # ragged K (zero-padded planes), narrower rows
+    (40, 1000, 1024, 3, 4, 1, 1),   # split K, ragged second half
+    (48, 264, 7168, 2, 3, -1, 0),   # split K, a second half of one k-step
+    (1, 8, 7168, 1, 1, -1, 1),      # K of one piece
+    (24, 2056, 520, 2, 3, 2, 1),    # two token tiles, ragged last row group
+])
+def test_packed_edges(M, K, H, nb, cap, write, has_delta):
+    s = synth.decode_step(M, K, nb, H=H, cap=cap, write=write, has_delta=has_delta,
+                          seed=500 + M + K)
+    a = _run(s, packed=True, final=0)
+    if M <= 32:
+        b = _run(s, packed=False, final=0)
+        for k in ("out", "prefix", "blocks", "aux"):
+            assert np.array_equal(a[k], b[k]), f"M={M} K={K} H={H}: {k} differs"
+    check_fused_step(x=s.x, W=s.W, old_prefix=s.prefix, blocks=s.blocks, norm=s.norm,
+                     query=s.query, out_norm=s.out_norm, nb=nb, write=write, has_delta=has_delta,
+                     final=0, eps=s.eps, out_eps=s.out_eps, gpu_out=a["out"], gpu_new=a["prefix"],
+                     what=f"packed M={M} K={K} H={H}")
