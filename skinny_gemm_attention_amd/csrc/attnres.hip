@@ -143,9 +143,9 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
     const int c = tid + j * NT;
     if (c < CH) {
       const size_t col = (size_t)c * 8;
-      st16(a.prefix + t * a.ld_prefix + col, nbits[j]);
-      if (a.aux) st16(a.aux + t * a.ld_aux + col, nbits[j]);
-      if (a.write >= 0) st16(a.blocks + t * a.bst_t + a.write * a.bst_b + col, nbits[j]);
+      st16_nt(a.prefix + t * a.ld_prefix + col, nbits[j]);
+      if (a.aux) st16_nt(a.aux + t * a.ld_aux + col, nbits[j]);
+      if (a.write >= 0) st16_nt(a.blocks + t * a.bst_t + a.write * a.bst_b + col, nbits[j]);
     }
   }
 
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(NT) void attnres_kernel(AttnParams a) {
       mg[j][i] = mix[j][i] * gg[j][i];
     }
   }
-  finish_out<NT, NCH>(a, t, out_coefs(a, pre, pp), nw, ng, mix, mg, gg, lds_fin);
+  finish_out<NT, NCH, false>(a, t, out_coefs(a, pre, pp), nw, ng, mix, mg, gg, lds_fin);
 }
 
 hipError_t launch_attnres(const AttnParams& p, hipStream_t stream) {

@@ -87,27 +87,39 @@ constexpr int kCacheNTLoad = 2;               // buffer-load cache policy: non-t
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
-// Output stores are non-temporal: every tensor a kernel writes is read by a
-// later kernel, not by this one (measured: attnres_run 7-13% faster at T=256).
-__device__ __forceinline__ void st16(void* p, u32x4 v) {
+// Output stores. Every tensor a kernel writes is read by a later kernel, not
+// by this one, so no output store keeps its line in the caches:
+//   * st16_nt: non-temporal (streaming) 16-byte store;
+//   * st4_wt / st8_wt / st16_wt: written through to memory (device scope: sc1
+//     global stores, issued as relaxed agent-scope atomic stores of 4 or 8
+//     bytes), which leaves no dirty line in the L2 caches for the release at
+//     the end of the kernel to write back. A 256-workgroup kernel storing
+//     1 MiB took 0.2 us longer per launch with plain or non-temporal stores,
+//     0.02 us with written-through ones; but written-through stores drain
+//     slower, so a kernel that stores tens of KiB per workgroup (attnres_run:
+//     5.4 -> 12.1 us at 256 tokens) keeps the non-temporal ones.
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
-__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
-__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
-
-// Device-scope (agent) 8-byte store and load. On gfx950 these are global
-// stores / loads with the device scope bit (sc1): they are coherent across the
-// L2 caches of the eight XCDs without writing back or invalidating any cache.
-__device__ __forceinline__ void st8_device(void* p, u32x2 v) {
+__device__ __forceinline__ void st4_wt(void* p, unsigned v) {
+  __hip_atomic_store(reinterpret_cast<unsigned*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st8_wt(void* p, u32x2 v) {
   __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
                      __builtin_bit_cast(unsigned long long, v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ u32x2 ld8_device(const void* p) {
-  return __builtin_bit_cast(
-      u32x2, __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT));
+__device__ __forceinline__ void st16_wt(void* p, u32x4 v) {
+  st8_wt(p, u32x2{v.x, v.y});
+  st8_wt(reinterpret_cast<char*>(p) + 8, u32x2{v.z, v.w});
 }
+// One of the two, chosen at compile time by the kernel.
+template <bool WT>
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  if constexpr (WT) st16_wt(p, v);
+  else st16_nt(p, v);
+}
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 // Blocks until every memory operation this wavefront has issued is complete:
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone). A completed device-scope

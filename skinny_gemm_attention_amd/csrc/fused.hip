@@ -52,10 +52,6 @@ namespace attnres {
 
 constexpr int kMaxTokensPerOwner = 2;
 
-__device__ __forceinline__ void st4_device(void* p, unsigned v) {
-  __hip_atomic_store(reinterpret_cast<unsigned*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ __forceinline__ void load_mix(const float* row, int c, bool valid, float (&m)[8]) {
   if (valid) {
     const f32x4* pm = reinterpret_cast<const f32x4*>(row + c * 8);
@@ -82,6 +78,11 @@ template <int RT, int TT, bool SPLIT, bool AHEAD, bool PACKED>
 __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, int NO) {
   constexpr int NT = kTokenThreads, NW = NT / 64;
   using C = typename FusedCore<SPLIT, RT, TT, PACKED>::type;
+  // outputs written through up to 32 tokens (one token, K = 1024 and eight
+  // tokens, K = 4096: 0.15 and 0.42 us faster per step); beyond, with four
+  // times the bytes per workgroup, non-temporal (written through was 0.08 us
+  // slower at 64 tokens)
+  constexpr bool WT = !SPLIT;
   static_assert(C::NT == NT, "one workgroup shape for both roles");
   // tokens per owner: one up to 32 tokens, two beyond
   constexpr int KT = TT <= 2 ? 1 : kMaxTokensPerOwner;
@@ -245,9 +246,9 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
             __builtin_amdgcn_make_buffer_rsrc(f.mailbox, 0, M * a.H * 2, kBufferDword3);
         __builtin_amdgcn_raw_buffer_store_b128(nv, mb, (unsigned)((size_t)om * a.H + col) * 2u, 0,
                                                kCacheSC1);  // collected by token om's owner
-        st16(a.prefix + (size_t)om * a.ld_prefix + col, nv);
-        if (a.aux) st16(a.aux + (size_t)om * a.ld_aux + col, nv);
-        if (a.write >= a.nb) st16(a.blocks + om * a.bst_t + a.write * a.bst_b + col, nv);
+        st16<WT>(a.prefix + (size_t)om * a.ld_prefix + col, nv);
+        if (a.aux) st16<WT>(a.aux + (size_t)om * a.ld_aux + col, nv);
+        if (a.write >= a.nb) st16<WT>(a.blocks + om * a.bst_t + a.write * a.bst_b + col, nv);
       }
       // re-arm the first workgroup's partials after the stores the owners wait
       // for (before them, the mailbox posts queued behind 16 KB of re-arm
@@ -274,12 +275,12 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
           nv = u32x2{y01, y23};
         }
         unsigned* box = f.mailbox + (size_t)qm[i] * (a.H >> 1) + ((row0 + qr[i]) >> 1);
-        st4_device(box, nv.x);  // collected by token qm's owner
-        if (qr[i] + 2 < rows) st4_device(box + 1, nv.y);
-        store_quad_pairs(a.prefix + (size_t)qm[i] * a.ld_prefix + row0, qr[i], rows, nv);
-        if (a.aux) store_quad_pairs(a.aux + (size_t)qm[i] * a.ld_aux + row0, qr[i], rows, nv);
+        st4_wt(box, nv.x);  // collected by token qm's owner
+        if (qr[i] + 2 < rows) st4_wt(box + 1, nv.y);
+        store_quad_pairs<WT>(a.prefix + (size_t)qm[i] * a.ld_prefix + row0, qr[i], rows, nv);
+        if (a.aux) store_quad_pairs<WT>(a.aux + (size_t)qm[i] * a.ld_aux + row0, qr[i], rows, nv);
         if (a.write >= a.nb)
-          store_quad_pairs(a.blocks + qm[i] * a.bst_t + a.write * a.bst_b + row0, qr[i], rows, nv);
+          store_quad_pairs<WT>(a.blocks + qm[i] * a.bst_t + a.write * a.bst_b + row0, qr[i], rows, nv);
       }
     }
     return;
@@ -317,8 +318,8 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
       if constexpr (AHEAD) {
         // the next layer's statistics over the same (launch-time) saved
         // blocks, stored for its post (oproj.prepared page, bind_ahead);
-        // non-temporal stores: a later kernel reads them (normal stores cost
-        // about 2 us at 64 tokens)
+        // written through like every output (a later kernel reads them;
+        // plain stores cost about 2 us at 64 tokens)
         float mix2[NCH][8];
         BlockStats pre2;
         token_pre2<NT, NCH>(a, t, w, w2, f.ah.eps, mix, mix2, pre[k], pre2, lds_pre);
@@ -327,12 +328,12 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
           const int c = tid + j * NT;
           if (c < CH && !flagw) {
             float* dst = f.ah.mix + (size_t)t * f.ah.ld_mix + (size_t)c * 8;
-            __builtin_nontemporal_store(f32x4{mix2[j][0], mix2[j][1], mix2[j][2], mix2[j][3]}, reinterpret_cast<f32x4*>(dst));
-            __builtin_nontemporal_store(f32x4{mix2[j][4], mix2[j][5], mix2[j][6], mix2[j][7]}, reinterpret_cast<f32x4*>(dst + 4));
+            st16<WT>(dst, __builtin_bit_cast(u32x4, f32x4{mix2[j][0], mix2[j][1], mix2[j][2], mix2[j][3]}));
+            st16<WT>(dst + 4, __builtin_bit_cast(u32x4, f32x4{mix2[j][4], mix2[j][5], mix2[j][6], mix2[j][7]}));
           }
         }
         if (tid == 0 && !flagw)
-          st8(f.ah.scal + 2 * (size_t)t, __builtin_bit_cast(u32x2, f32x2{pre2.anchor, pre2.total}));
+          st8_wt(f.ah.scal + 2 * (size_t)t, __builtin_bit_cast(u32x2, f32x2{pre2.anchor, pre2.total}));
       } else {
         pre[k] = token_pre<NT, NCH>(a, t, w, mix, lds_pre);
       }
@@ -500,11 +501,11 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
           const int c = tid + j * NT;
-          if (c < CH) st16(a.blocks + t * a.bst_t + a.write * a.bst_b + (size_t)c * 8, nbits[k][j]);
+          if (c < CH) st16<WT>(a.blocks + t * a.bst_t + a.write * a.bst_b + (size_t)c * 8, nbits[k][j]);
         }
       }
       const float tot[4] = {pp[4 * k], pp[4 * k + 1], pp[4 * k + 2], pp[4 * k + 3]};
-      finish_out<NT, NCH>(a, t, out_coefs(a, pre[k], tot), nw, ng, mix, mg, gg, lds_fin);
+      finish_out<NT, NCH, WT>(a, t, out_coefs(a, pre[k], tot), nw, ng, mix, mg, gg, lds_fin);
       if (a.final_b) lds_barrier();  // lds_fin is reused by the next token
     }
   }

@@ -397,10 +397,16 @@ __host__ __device__ inline int gemm_rows_per_wg(int N) {
 
 // The epilogue of quad q: rows r .. r+3 of token m, stored as two bf16 pairs;
 // the row count of a workgroup is even, so each pair is all-in or all-out.
-// Non-temporal, like every output store (a later kernel reads them).
+// Written through (WT) or non-temporal (a later kernel reads them).
+template <bool WT>
 __device__ __forceinline__ void store_quad_pairs(uint16_t* row, int r, int rows, u32x2 v) {
-  if (r < rows) __builtin_nontemporal_store(v.x, reinterpret_cast<unsigned*>(row + r));
-  if (r + 2 < rows) __builtin_nontemporal_store(v.y, reinterpret_cast<unsigned*>(row + r + 2));
+  if constexpr (WT) {
+    if (r < rows) st4_wt(row + r, v.x);
+    if (r + 2 < rows) st4_wt(row + r + 2, v.y);
+  } else {
+    if (r < rows) __builtin_nontemporal_store(v.x, reinterpret_cast<unsigned*>(row + r));
+    if (r + 2 < rows) __builtin_nontemporal_store(v.y, reinterpret_cast<unsigned*>(row + r + 2));
+  }
 }
 
 }  // namespace attnres

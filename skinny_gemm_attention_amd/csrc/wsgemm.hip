@@ -27,7 +27,7 @@ __global__ __launch_bounds__(512) void wsgemm_kernel(GemmParams p, int R) {
       const f32x4 s = C::gather(red, q);
       const u32x2 v = {positive_zero(pack2(s.x, s.y)), positive_zero(pack2(s.z, s.w))};
       if (!p.moe) {
-        store_quad_pairs(p.y + (size_t)m * p.ldy + row0, r, rows, v);
+        store_quad_pairs<false>(p.y + (size_t)m * p.ldy + row0, r, rows, v);
       } else {
         // valid and split are multiples of 8 and a quad's four rows start at
         // a multiple of 4: the whole quad falls in one shard
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(512) void wsgemm_kernel(GemmParams p, int R) {
           __builtin_nontemporal_store(w.z == kMailboxSentinel ? 0u : w.z, dst + 2);
           __builtin_nontemporal_store(w.w == kMailboxSentinel ? 0u : w.w, dst + 3);
         } else if (c >= p.split) {  // latent shard: bf16 at base + c - split
-          store_quad_pairs(orow + p.base + (row0 - p.split), r, rows, v);
+          store_quad_pairs<false>(orow + p.base + (row0 - p.split), r, rows, v);
         }
       }
     }
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(512) void wsgemm_split_kernel(GemmParams p, unsigne
   for (int it = tid; it < p.M * 8; it += C::NT) {  // 16 bytes (8 rows) of one token each
     const int om = it >> 3, oj = it & 7;
     if (8 * oj < rows)
-      st16(p.y + (size_t)om * p.ldy + row0 + 8 * oj,
+      st16_nt(p.y + (size_t)om * p.ldy + row0 + 8 * oj,
            *reinterpret_cast<const u32x4*>(tile + om * (kSplitRows / 2) + 4 * oj));
   }
 }
