@@ -56,7 +56,14 @@ FOOTPRINT = 640e6
 # code (comments and whitespace aside), and roofline.traffic is null when the
 # sources differ.
 KERNEL_SOURCES = ("common.hpp", "token.hpp", "gemm.hpp", "launch.hpp", "fused.hip")
-MEASURED_TRAFFIC = {}  # (workload, "prepared" | "row-major") -> {"digest", "fetch", "write"}
+MEASURED_TRAFFIC = {  # (workload, "prepared" | "row-major") -> {"digest", "fetch", "write"}
+    (1, "prepared"): {"digest": "77d051b1ab7da6c2d25c12d8f322d17e7524a8ad1b3ff2a3c798aa9df7aa5842", "fetch": 61038201, "write": 1583616},
+    (1, "row-major"): {"digest": "77d051b1ab7da6c2d25c12d8f322d17e7524a8ad1b3ff2a3c798aa9df7aa5842", "fetch": 61039804, "write": 1583616},
+    (0, "prepared"): {"digest": "77d051b1ab7da6c2d25c12d8f322d17e7524a8ad1b3ff2a3c798aa9df7aa5842", "fetch": 14996643, "write": 197952},
+    (0, "row-major"): {"digest": "77d051b1ab7da6c2d25c12d8f322d17e7524a8ad1b3ff2a3c798aa9df7aa5842", "fetch": 14992718, "write": 197952},
+    (2, "prepared"): {"digest": "77d051b1ab7da6c2d25c12d8f322d17e7524a8ad1b3ff2a3c798aa9df7aa5842", "fetch": 139267779, "write": 9175040},
+    (2, "row-major"): {"digest": "77d051b1ab7da6c2d25c12d8f322d17e7524a8ad1b3ff2a3c798aa9df7aa5842", "fetch": 139130706, "write": 9175040},
+}
 
 WORKLOADS = {
     0: dict(M=1, K=1024, nb=1, cap=1, write=-1, has_delta=1),
@@ -552,7 +559,9 @@ def main():
             "unit": "GB/s",
             "frac": f["frac"],
             "traffic": f["traffic"],
-            "kernel": "fused_kernel (attnres_oproj_run), one launch per step",
+            "kernel": ("fused_packed_kernel (attnres_oproj_packed_run on W prepared by attnres_pack_weights)"
+                       if f["w_layout"] == "prepared" else "fused_kernel (attnres_oproj_run)")
+                      + ", one launch per step",
             "algorithmic_bytes_per_launch": f["algorithmic_bytes_per_launch"],
             "traffic_note": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated); "
                             "null unless measured on these kernel sources",
