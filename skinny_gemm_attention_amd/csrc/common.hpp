@@ -89,7 +89,7 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 }
 // Output stores. Every tensor a kernel writes is read by a later kernel, not
 // by this one, so no output store keeps its line in the caches:
-//   * st16_nt: non-temporal (streaming) 16-byte store;
+//   * st16_nt / st8_nt: non-temporal (streaming) 16- or 8-byte store;
 //   * st4_wt / st8_wt / st16_wt: written through to memory (device scope: sc1
 //     global stores, issued as relaxed agent-scope atomic stores of 4 or 8
 //     bytes), which leaves no dirty line in the L2 caches for the release at
@@ -100,6 +100,9 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 //     5.4 -> 12.1 us at 256 tokens) keeps the non-temporal ones.
 __device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void st8_nt(void* p, u32x2 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
 }
 __device__ __forceinline__ void st4_wt(void* p, unsigned v) {
   __hip_atomic_store(reinterpret_cast<unsigned*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

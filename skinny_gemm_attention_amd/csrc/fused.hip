@@ -296,7 +296,8 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
   // nonzero: an earlier call on this workspace gave up a wait, so this call
   // writes nothing. Each wavefront reads it and returns as a whole before its
   // first store; a wavefront that has ended no longer takes part in the
-  // workgroup's barriers, so the others never wait for it.
+  // workgroup's barriers, so the others never wait for it. (Taking its value
+  // only after pre() was 0.07-0.15 us slower per step.)
   const unsigned flagw = __builtin_amdgcn_readfirstlane(
       __hip_atomic_load(&f.ws->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   float gg[NCH][8], w[NCH][8], w2[AHEAD ? NCH : 1][8];
@@ -318,8 +319,9 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
       if constexpr (AHEAD) {
         // the next layer's statistics over the same (launch-time) saved
         // blocks, stored for its post (oproj.prepared page, bind_ahead);
-        // written through like every output (a later kernel reads them;
-        // plain stores cost about 2 us at 64 tokens)
+        // non-temporal (a later kernel reads them; plain stores cost about
+        // 2 us at 64 tokens, and written through, the owner's polls behind
+        // them waited for their slower completion: 1.1 us at one token)
         float mix2[NCH][8];
         BlockStats pre2;
         token_pre2<NT, NCH>(a, t, w, w2, f.ah.eps, mix, mix2, pre[k], pre2, lds_pre);
@@ -328,12 +330,12 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
           const int c = tid + j * NT;
           if (c < CH && !flagw) {
             float* dst = f.ah.mix + (size_t)t * f.ah.ld_mix + (size_t)c * 8;
-            st16<WT>(dst, __builtin_bit_cast(u32x4, f32x4{mix2[j][0], mix2[j][1], mix2[j][2], mix2[j][3]}));
-            st16<WT>(dst + 4, __builtin_bit_cast(u32x4, f32x4{mix2[j][4], mix2[j][5], mix2[j][6], mix2[j][7]}));
+            st16_nt(dst, __builtin_bit_cast(u32x4, f32x4{mix2[j][0], mix2[j][1], mix2[j][2], mix2[j][3]}));
+            st16_nt(dst + 4, __builtin_bit_cast(u32x4, f32x4{mix2[j][4], mix2[j][5], mix2[j][6], mix2[j][7]}));
           }
         }
         if (tid == 0 && !flagw)
-          st8_wt(f.ah.scal + 2 * (size_t)t, __builtin_bit_cast(u32x2, f32x2{pre2.anchor, pre2.total}));
+          st8_nt(f.ah.scal + 2 * (size_t)t, __builtin_bit_cast(u32x2, f32x2{pre2.anchor, pre2.total}));
       } else {
         pre[k] = token_pre<NT, NCH>(a, t, w, mix, lds_pre);
       }

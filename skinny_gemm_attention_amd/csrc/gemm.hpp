@@ -300,15 +300,17 @@ struct GemmLds {
   }
 
   // Consumes every chunk; returns with all loads complete and all wavefronts
-  // past their last LDS read of the ring. Up to two token tiles the loop is
-  // software-pipelined by one chunk: the products of chunk c - 1 run while
-  // chunk c's fragment reads are in flight (two fragment sets in turn; the
-  // products keep chunk order). Wider tiles (twice the fragment registers)
-  // read and multiply each chunk in turn: written as load_frags + mma, that
-  // loop made the compiler wait for the chunk's own LDS traffic before its
-  // fragment reads (64 tokens, K = 8192: 31.0 -> 36.8 us).
+  // past their last LDS read of the ring. With two row tiles and up to two
+  // token tiles the loop is software-pipelined by one chunk: the products of
+  // chunk c - 1 run while chunk c's fragment reads are in flight (two
+  // fragment sets in turn; the products keep chunk order). Other tiles read
+  // and multiply each chunk in turn: written as load_frags + mma, that loop
+  // made the compiler wait for the chunk's own LDS traffic before its
+  // fragment reads at four token tiles (64 tokens, K = 8192: 31.0 -> 36.8 us),
+  // and the 16-row tile of 1 KiB segments ran 0.4 us slower pipelined
+  // (8 tokens, K = 7168, N = 4096).
   __device__ __forceinline__ void finish() {
-    if (TT > 2) {
+    if (TT > 2 || RT == 1) {
       for (int c = 0; c < nC; ++c) {
         const int ahead = min(c + NSLOT - 2, nC - 1) - c;  // chunks after c already issued
         wait_vmem_upto<MAXSEG * (NSLOT - 2)>(nseg * ahead);
