@@ -78,10 +78,12 @@ template <int RT, int TT, bool SPLIT, bool AHEAD, bool PACKED>
 __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, int NO) {
   constexpr int NT = kTokenThreads, NW = NT / 64;
   using C = typename FusedCore<SPLIT, RT, TT, PACKED>::type;
-  // outputs written through up to 32 tokens (one token, K = 1024 and eight
-  // tokens, K = 4096: 0.15 and 0.42 us faster per step); beyond, with four
-  // times the bytes per workgroup, non-temporal (written through was 0.08 us
-  // slower at 64 tokens)
+  // the GEMM role's outputs written through up to 32 tokens (one token,
+  // K = 1024 and eight tokens, K = 4096: 0.15 and 0.42 us faster per step);
+  // beyond, with four times the bytes per workgroup, non-temporal (written
+  // through was 0.08 us slower at 64 tokens). The owners' output rows are
+  // non-temporal at every size: their completion ends the step, and the L2
+  // acknowledges a non-temporal store sooner (0.02-0.04 us per step).
   constexpr bool WT = !SPLIT;
   static_assert(C::NT == NT, "one workgroup shape for both roles");
   // tokens per owner: one up to 32 tokens, two beyond
@@ -162,10 +164,12 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
     }
     if (tid == 0) lds_flag = flag0;
     lds_barrier();
-    if (lds_flag) return;  // the whole workgroup: the same LDS word after the barrier
+    // the flag is read with the partials (one LDS round trip for both)
+    const unsigned flag = lds_flag;
     f32x4 s[QPT];
 #pragma unroll
     for (int i = 0; i < QPT; ++i) s[i] = qv[i] ? C::gather(red, tid + i * NT) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (flag) return;  // the whole workgroup: the same LDS word after the barrier
     if (SPLIT) {
       const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
           f.partials, 0, f.ng * C::kQuads * 16, kBufferDword3);
@@ -507,7 +511,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
         }
       }
       const float tot[4] = {pp[4 * k], pp[4 * k + 1], pp[4 * k + 2], pp[4 * k + 3]};
-      finish_out<NT, NCH, WT>(a, t, out_coefs(a, pre[k], tot), nw, ng, mix, mg, gg, lds_fin);
+      finish_out<NT, NCH, false>(a, t, out_coefs(a, pre[k], tot), nw, ng, mix, mg, gg, lds_fin);
       if (a.final_b) lds_barrier();  // lds_fin is reused by the next token
     }
   }
