@@ -259,7 +259,8 @@ def _line(metric, nbytes, us, workload, **extra):
 
 def lookahead_configs(args, np, torch, sga, synth, up, steps):
     """The fused step with and without the next layer's saved-block statistics
-    (mixture [M, H] FP32 + [M, 2] written on top), and AttnRes on carried
+    (mixture [M, H] FP32 + [M, 2] written on top), on row-major and on
+    prepared W, and AttnRes on carried
     statistics (reads the FP32 mixture instead of nb saved blocks) beside
     attnres_run."""
     dev = torch.device("cuda:0")
@@ -267,9 +268,10 @@ def lookahead_configs(args, np, torch, sga, synth, up, steps):
         M, K, nb, cap, write = (cfg[k] for k in ("M", "K", "nb", "cap", "write"))
         s = synth.decode_step(M, K, nb, cap=cap, write=write, seed=0)
         nx = synth.decode_step(1, None, 0, seed=0, layer=1)
-        copy_bytes = 2 * H * K + 2 * M * K + M * 2 * H * (4 + cap) + M * H * 4
+        copy_bytes = 2 * (2 * H * K) + 2 * M * K + M * 2 * H * (4 + cap) + M * H * 4  # W twice
         L = max(2, math.ceil(FOOTPRINT / copy_bytes))
         base = dict(x=up(s.x), W=up(s.W), prefix=up(s.prefix), blocks=up(s.blocks))
+        base["Wp"] = sga.attnres_pack_weights(base["W"])
         nq = [up(s.norm), up(s.query), up(s.out_norm)]
         nn, nqq = up(nx.norm), up(nx.query)
         layers = []
@@ -294,10 +296,24 @@ def lookahead_configs(args, np, torch, sga, synth, up, steps):
                                         t["aux"], t["ws"], nn, nqq, t["mix"], t["scal"], nb=nb,
                                         write=write)
 
+        def packed_plain(i):
+            t = layers[i % L]
+            sga.attnres_oproj_packed_run(t["x"], t["Wp"], H, t["prefix"], t["blocks"], *nq,
+                                         t["out"], t["aux"], t["ws"], nb=nb, write=write)
+
+        def packed_ahead(i):
+            t = layers[i % L]
+            sga.attnres_oproj_packed_ahead_run(t["x"], t["Wp"], H, t["prefix"], t["blocks"], *nq,
+                                               t["out"], t["aux"], t["ws"], nn, nqq, t["mix"],
+                                               t["scal"], nb=nb, write=write)
+
         base_bytes = algorithmic_bytes(M, K, nb, write, 1)
         extra = 2 * 2 * H + M * H * 4 + M * 8  # next norm + query, mixture, scal
         for name, fn, nbytes in (("attnres_oproj_run", plain, base_bytes),
-                                 ("attnres_oproj_ahead_run", ahead, base_bytes + extra)):
+                                 ("attnres_oproj_ahead_run", ahead, base_bytes + extra),
+                                 ("attnres_oproj_packed_run", packed_plain, base_bytes),
+                                 ("attnres_oproj_packed_ahead_run", packed_ahead,
+                                  base_bytes + extra)):
             us = graph_time_us(torch, fn, steps, args.warmup)
             _line(f"{name} µs/call + achieved HBM GB/s", nbytes, us,
                   f"{name} M={M} K={K} N=H={H} nb={nb} write={write}", layer_copies=L)

@@ -196,7 +196,7 @@ int attnres_oproj_workspace_init(void* workspace, size_t workspace_bytes, void* 
 
 /*
  * attnres_workspace_status - whether a wait of a call on this workspace
- * (attnres_oproj_run, attnres_oproj_ahead_run, wsgemm_run_ws) gave up: waits
+ * (attnres_oproj_run and its prepared-W and look-ahead forms, wsgemm_run_ws) gave up: waits
  * until the work enqueued on `stream` so far has finished (it synchronises
  * the host with the stream; not for use under stream capture), then reads the
  * workspace header. workspace == NULL with workspace_bytes == 0 names the
@@ -337,6 +337,28 @@ int attnres_oproj_ahead_run(const void* x, int64_t ldx, const void* W, int64_t l
                             const void* next_norm, const void* next_query, float next_eps,
                             float* mixture, int64_t ld_mixture, float* scal, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * attnres_oproj_packed_ahead_run - attnres_oproj_ahead_run with W given in the
+ * prepared layout (oproj.prepared page: the prepared object is the one that
+ * binds the look-ahead, PreparedOproj.bind_ahead). Wp and Wp_bytes as for
+ * attnres_oproj_packed_run; next_norm, next_query, next_eps, mixture,
+ * ld_mixture and scal as for attnres_oproj_ahead_run. The statistics equal
+ * attnres_oproj_ahead_run's bit for bit (they do not involve W); the other
+ * outputs relate to attnres_oproj_ahead_run's as attnres_oproj_packed_run's
+ * relate to attnres_oproj_run's.
+ * Errors: those of attnres_oproj_packed_run and attnres_oproj_ahead_run.
+ */
+int attnres_oproj_packed_ahead_run(const void* x, int64_t ldx, const void* Wp, size_t Wp_bytes,
+                                   int K, void* prefix, int64_t ld_prefix, void* blocks,
+                                   int64_t blk_stride_t, int64_t blk_stride_b, int cap,
+                                   const void* norm, const void* query, const void* out_norm,
+                                   void* out, int64_t ld_out, void* aux, int64_t ld_aux, float eps,
+                                   float out_eps, int M, int H, int nb, int write, int has_delta,
+                                   int final_boundary, const void* next_norm,
+                                   const void* next_query, float next_eps, float* mixture,
+                                   int64_t ld_mixture, float* scal, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /*
  * attnres_post_run - attnres_run on carried saved-block statistics instead of

@@ -57,6 +57,10 @@ _lib.attnres_oproj_run_noalloc.argtypes = [_P, _I64, _P, _I64, _I, _P, _I64, _P,
 _lib.attnres_oproj_ahead_run.argtypes = [_P, _I64, _P, _I64, _I, _P, _I64, _P, _I64, _I64, _I,
                                          _P, _P, _P, _P, _I64, _P, _I64, _F, _F, _I, _I, _I, _I,
                                          _I, _I, _P, _P, _F, _P, _I64, _P, _P, _SZ, _P]
+_lib.attnres_oproj_packed_ahead_run.argtypes = [_P, _I64, _P, _SZ, _I, _P, _I64, _P, _I64, _I64,
+                                                _I, _P, _P, _P, _P, _I64, _P, _I64, _F, _F, _I,
+                                                _I, _I, _I, _I, _I, _P, _P, _F, _P, _I64, _P, _P,
+                                                _SZ, _P]
 _lib.attnres_post_run.argtypes = [_P, _I64, _P, _I64, _P, _I64, _I64, _I, _P, _P, _P, _P, _I64,
                                   _P, _I64, _P, _I64, _P, _F, _F, _I, _I, _I, _I, _I, _I, _P]
 _lib.attnres_workspace_status.argtypes = [_P, _SZ, _P]
@@ -67,7 +71,8 @@ _lib.attnres_strerror.argtypes = [_I]
 _lib.attnres_strerror.restype = ctypes.c_char_p
 for _f in (_lib.attnres_run, _lib.wsgemm_run, _lib.wsgemm_run_ws, _lib.wsgemm_moe_front_run,
            _lib.attnres_oproj_run, _lib.attnres_oproj_run_noalloc,
-           _lib.attnres_oproj_ahead_run, _lib.attnres_post_run):
+           _lib.attnres_oproj_ahead_run, _lib.attnres_oproj_packed_ahead_run,
+           _lib.attnres_post_run):
     _f.restype = _I
 
 EXPORTS = ("attnres_run", "wsgemm_run", "wsgemm_moe_front_run", "wsgemm_workspace_size",
@@ -76,7 +81,7 @@ EXPORTS = ("attnres_run", "wsgemm_run", "wsgemm_moe_front_run", "wsgemm_workspac
            "attnres_oproj_workspace_init", "attnres_oproj_ahead_run", "attnres_post_run",
            "attnres_strerror", "attnres_stream_read", "attnres_workspace_status",
            "attnres_oproj_run_noalloc", "attnres_packed_weights_size", "attnres_pack_weights",
-           "attnres_oproj_packed_run")
+           "attnres_oproj_packed_run", "attnres_oproj_packed_ahead_run")
 
 STREAM_READ_SINK_WORDS = 65536  # ATTNRES_STREAM_READ_SINK_WORDS
 EWAIT = -7  # ATTNRES_EWAIT: a wait of an earlier call on the workspace gave up
@@ -431,6 +436,39 @@ def attnres_oproj_ahead_run(x, W, prefix, blocks, norm, query, out_norm, out, au
         _fptr(mixture), 0 if mixture is None else mixture.stride(0), _fptr(scal), ws, wsb,
         _stream(stream))
     _check(rc, "attnres_oproj_ahead_run")
+    return out, prefix, blocks, mixture, scal
+
+
+def attnres_oproj_packed_ahead_run(x, Wp, H, prefix, blocks, norm, query, out_norm, out, aux,
+                                   workspace, next_norm, next_query, mixture, scal, *, nb,
+                                   write=-1, has_delta=1, final_boundary=0, eps=1e-6, out_eps=1e-6,
+                                   next_eps=1e-6, stream=None):
+    """attnres_oproj_ahead_run with W [H, K] given as attnres_pack_weights(W)."""
+    M, K = x.shape
+    _attn_shapes(M, H, prefix, blocks, norm, query, out_norm, out, aux)
+    have = Wp.numel() * Wp.element_size()
+    if have < attnres_packed_weights_size(H, K):
+        raise AttnResError(-1, f"Wp must hold >= {attnres_packed_weights_size(H, K)} bytes")
+    if not Wp.is_cuda:
+        raise AttnResError(-1, "tensors must be on the GPU")
+    _vec(next_norm, H, "next_norm")
+    _vec(next_query, H, "next_query")
+    _rows(mixture, M, H, "mixture")
+    if scal is not None and scal.numel() < 2 * M:
+        raise AttnResError(-1, f"scal must hold >= {2 * M} floats")
+    if mixture is not None and mixture.stride(-1) != 1:
+        raise AttnResError(-1, "mixture rows must be contiguous")
+    bst_t, bst_b, cap = _block_strides(blocks)
+    ws = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.attnres_oproj_packed_ahead_run(
+        _ptr(x), _row_stride(x), ctypes.c_void_p(Wp.data_ptr()), have, K, _ptr(prefix),
+        _row_stride(prefix), _ptr(blocks), bst_t, bst_b, cap, _ptr(norm), _ptr(query),
+        _ptr(out_norm), _ptr(out), _row_stride(out), _ptr(aux), _row_stride(aux), eps, out_eps, M,
+        H, nb, write, int(has_delta), int(final_boundary), _ptr(next_norm), _ptr(next_query),
+        next_eps, _fptr(mixture), 0 if mixture is None else mixture.stride(0), _fptr(scal), ws,
+        wsb, _stream(stream))
+    _check(rc, "attnres_oproj_packed_ahead_run")
     return out, prefix, blocks, mixture, scal
 
 

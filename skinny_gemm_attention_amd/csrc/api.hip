@@ -317,6 +317,25 @@ int static_workspace_if_used(hipStream_t stream, void** ws) {
   return ATTNRES_OK;
 }
 
+// Checks of the look-ahead arguments (attnres_oproj_ahead_run and its
+// prepared-W form); fills `ah` when they pass.
+int ahead_params(const void* next_norm, const void* next_query, float next_eps, float* mixture,
+                 int64_t ld_mixture, float* scal, int H, attnres::AheadParams* ah) {
+  if (!next_norm || !next_query || !mixture || !scal) return ATTNRES_EINVAL;
+  if (!(next_eps >= 0.0f) || next_eps > 1e30f) return ATTNRES_EINVAL;
+  if (H >= 8 && H <= ATTNRES_MAX_H && !(H & 7)) {  // other H: rejected by the fused checks
+    if (ld_mixture < H) return ATTNRES_EINVAL;
+  }
+  if (!aligned16(next_norm) || !aligned16(next_query) || !aligned16(mixture) ||
+      (reinterpret_cast<uintptr_t>(scal) & 7u))
+    return ATTNRES_EALIGN;
+  if (!stride8(ld_mixture)) return ATTNRES_EALIGN;
+  *ah = attnres::AheadParams{static_cast<const uint16_t*>(next_norm),
+                             static_cast<const uint16_t*>(next_query), next_eps, mixture,
+                             ld_mixture, scal};
+  return ATTNRES_OK;
+}
+
 // Checks and launch of the fused call; with `library_ws` the workspace is the
 // library's own (attnres_oproj_run_noalloc) and `workspace` is ignored.
 int oproj_common(const void* x, int64_t ldx, const void* W, int64_t ldw, int K, void* prefix,
@@ -440,22 +459,32 @@ int attnres_oproj_ahead_run(const void* x, int64_t ldx, const void* W, int64_t l
                             const void* next_norm, const void* next_query, float next_eps,
                             float* mixture, int64_t ld_mixture, float* scal, void* workspace,
                             size_t workspace_bytes, void* stream) {
-  if (!next_norm || !next_query || !mixture || !scal) return ATTNRES_EINVAL;
-  if (!(next_eps >= 0.0f) || next_eps > 1e30f) return ATTNRES_EINVAL;
-  if (H >= 8 && H <= ATTNRES_MAX_H && !(H & 7)) {  // other H: rejected below
-    if (ld_mixture < H) return ATTNRES_EINVAL;
-  }
-  if (!aligned16(next_norm) || !aligned16(next_query) || !aligned16(mixture) ||
-      (reinterpret_cast<uintptr_t>(scal) & 7u))
-    return ATTNRES_EALIGN;
-  if (!stride8(ld_mixture)) return ATTNRES_EALIGN;
-  attnres::AheadParams ah = {static_cast<const uint16_t*>(next_norm),
-                             static_cast<const uint16_t*>(next_query), next_eps, mixture,
-                             ld_mixture, scal};
+  attnres::AheadParams ah;
+  const int rc = ahead_params(next_norm, next_query, next_eps, mixture, ld_mixture, scal, H, &ah);
+  if (rc) return rc;
   return oproj_common(x, ldx, W, ldw, K, prefix, ld_prefix, blocks, blk_stride_t, blk_stride_b,
                       cap, norm, query, out_norm, out, ld_out, aux, ld_aux, eps, out_eps, M, H,
                       nb, write, has_delta, final_boundary, workspace, workspace_bytes, ah,
                       stream);
+}
+
+int attnres_oproj_packed_ahead_run(const void* x, int64_t ldx, const void* Wp, size_t Wp_bytes,
+                                   int K, void* prefix, int64_t ld_prefix, void* blocks,
+                                   int64_t blk_stride_t, int64_t blk_stride_b, int cap,
+                                   const void* norm, const void* query, const void* out_norm,
+                                   void* out, int64_t ld_out, void* aux, int64_t ld_aux, float eps,
+                                   float out_eps, int M, int H, int nb, int write, int has_delta,
+                                   int final_boundary, const void* next_norm,
+                                   const void* next_query, float next_eps, float* mixture,
+                                   int64_t ld_mixture, float* scal, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  attnres::AheadParams ah;
+  const int rc = ahead_params(next_norm, next_query, next_eps, mixture, ld_mixture, scal, H, &ah);
+  if (rc) return rc;
+  return oproj_common(x, ldx, Wp, 0, K, prefix, ld_prefix, blocks, blk_stride_t, blk_stride_b,
+                      cap, norm, query, out_norm, out, ld_out, aux, ld_aux, eps, out_eps, M, H,
+                      nb, write, has_delta, final_boundary, workspace, workspace_bytes, ah, stream,
+                      false, true, Wp_bytes);
 }
 
 int attnres_post_run(const void* delta, int64_t ld_delta, void* prefix, int64_t ld_prefix,

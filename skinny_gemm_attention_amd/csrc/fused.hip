@@ -517,7 +517,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
   }
 }
 
-// Three kernel templates over one body (rather than one kernel template with
+// Four kernel templates over one body (rather than one kernel template with
 // look-ahead and W-layout flags): hipcc emitted the host launch stub of only
 // one of two kernel instantiations that differed in nothing but such a flag.
 template <int RT, int TT, bool SPLIT>
@@ -531,11 +531,18 @@ __global__ __launch_bounds__(kTokenThreads) void fused_ahead_kernel(FusedParams 
   fused_body<RT, TT, SPLIT, true, false>(f, R, G, NO);
 }
 
-// W in the prepared layout (attnres_oproj_packed_run; no look-ahead variant)
+// W in the prepared layout (attnres_oproj_packed_run), without and with the
+// look-ahead statistics (attnres_oproj_packed_ahead_run)
 template <int RT, int TT, bool SPLIT>
 __global__ __launch_bounds__(kTokenThreads) void fused_packed_kernel(FusedParams f, int R, int G,
                                                                       int NO) {
   fused_body<RT, TT, SPLIT, false, true>(f, R, G, NO);
+}
+
+template <int RT, int TT, bool SPLIT>
+__global__ __launch_bounds__(kTokenThreads) void fused_packed_ahead_kernel(FusedParams f, int R,
+                                                                            int G, int NO) {
+  fused_body<RT, TT, SPLIT, true, true>(f, R, G, NO);
 }
 
 __global__ void workspace_init_kernel(unsigned* ws, size_t words) {
@@ -571,7 +578,10 @@ namespace {
 
 template <int RT, int TT, bool SPLIT = false>
 hipError_t go(const FusedParams& p, int R, int G, int NO, hipStream_t stream) {
-  if (p.wrows > 0)
+  if (p.wrows > 0 && p.ah.mix)
+    hipLaunchKernelGGL((fused_packed_ahead_kernel<RT, TT, SPLIT>), dim3(G + NO),
+                       dim3(kTokenThreads), 0, stream, p, R, G, NO);
+  else if (p.wrows > 0)
     hipLaunchKernelGGL((fused_packed_kernel<RT, TT, SPLIT>), dim3(G + NO), dim3(kTokenThreads), 0,
                        stream, p, R, G, NO);
   else if (p.ah.mix)

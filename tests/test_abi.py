@@ -45,6 +45,9 @@ def lib():
     L.attnres_pack_weights.argtypes = [P, I64, I, I, P, SZ, P]
     L.attnres_oproj_packed_run.argtypes = [P, I64, P, SZ, I, P, I64, P, I64, I64, I, P, P, P, P,
                                            I64, P, I64, F, F, I, I, I, I, I, I, P, SZ, P]
+    L.attnres_oproj_packed_ahead_run.argtypes = [P, I64, P, SZ, I, P, I64, P, I64, I64, I, P, P,
+                                                 P, P, I64, P, I64, F, F, I, I, I, I, I, I, P, P,
+                                                 F, P, I64, P, P, SZ, P]
     L.attnres_workspace_status.argtypes = [P, SZ, P]
     L.attnres_workspace_status.restype = I
     L.attnres_stream_read.argtypes = [P, SZ, P, P]
@@ -68,7 +71,8 @@ def test_header_symbols_exported(lib):
                           "attnres_oproj_ahead_run", "attnres_post_run", "attnres_strerror",
                           "attnres_stream_read", "attnres_workspace_status",
                           "attnres_oproj_run_noalloc", "attnres_packed_weights_size",
-                          "attnres_pack_weights", "attnres_oproj_packed_run"}
+                          "attnres_pack_weights", "attnres_oproj_packed_run",
+                          "attnres_oproj_packed_ahead_run"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -392,3 +396,29 @@ def call_packed(lib, **kw):
 ])
 def test_attnres_oproj_packed_run_rejects(lib, change, code):
     assert call_packed(lib, **change) == code
+
+
+def call_packed_ahead(lib, **kw):
+    a = attn_args()
+    a.update(x=A, ldx=8192, Wp=A, wpb=7168 * 8192 * 2, K=8192, ws=A, wsb=256 + 4 * 7168 * 2, M=4,
+             nn=A, nq=A, neps=1e-6, mix=A, ldm=7168, scal=A)
+    a.update(kw)
+    return lib.attnres_oproj_packed_ahead_run(
+        a["x"], a["ldx"], a["Wp"], a["wpb"], a["K"], a["prefix"], a["ld_prefix"], a["blocks"],
+        a["bst_t"], a["bst_b"], a["cap"], a["norm"], a["query"], a["out_norm"], a["out"],
+        a["ld_out"], a["aux"], a["ld_aux"], a["eps"], a["out_eps"], a["M"], a["H"], a["nb"],
+        a["write"], a["has_delta"], a["final"], a["nn"], a["nq"], a["neps"], a["mix"], a["ldm"],
+        a["scal"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(x=None), -1), (dict(Wp=None), -1), (dict(M=0), -3), (dict(K=8190), -4),
+    (dict(wpb=7168 * 8192 * 2 - 256), -1), (dict(ws=None), -5),
+    (dict(nn=None), -1), (dict(nq=None), -1), (dict(mix=None), -1), (dict(scal=None), -1),
+    (dict(neps=-1.0), -1), (dict(ldm=7000), -1), (dict(mix=A + 8), -2), (dict(ldm=7172), -2),
+    (dict(scal=A + 4), -2),
+])
+def test_attnres_oproj_packed_ahead_run_rejects(lib, change, code):
+    """Host-side rejections only (the fake pointers are never dereferenced)."""
+    assert call_packed_ahead(lib, **change) == code
+

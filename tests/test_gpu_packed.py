@@ -121,3 +121,55 @@ def test_packed_edges(M, K, H, nb, cap, write, has_delta):
                      query=s.query, out_norm=s.out_norm, nb=nb, write=write, has_delta=has_delta,
                      final=0, eps=s.eps, out_eps=s.out_eps, gpu_out=a["out"], gpu_new=a["prefix"],
                      what=f"packed M={M} K={K} H={H}")
+
+
+def _run_ahead(s, nn, nq, *, packed, final, pad=8):
+    """attnres_oproj_packed_ahead_run (packed) or attnres_oproj_ahead_run."""
+    sga = lib()
+    prefix, blocks = up(s.prefix), up(s.blocks)
+    out = torch.full((s.M, s.H), POISON, dtype=torch.int16, device=DEV)
+    aux = torch.full((s.M, s.H), POISON, dtype=torch.int16, device=DEV)
+    ws = sga.make_workspace(s.M, s.H, s.nb, DEV)
+    mix = torch.full((s.M, s.H + pad), float("nan"), dtype=torch.float32, device=DEV)
+    scal = torch.full((s.M, 2), float("nan"), dtype=torch.float32, device=DEV)
+    kw = dict(nb=s.nb, write=s.write, has_delta=s.has_delta, final_boundary=final, eps=s.eps,
+              out_eps=s.out_eps, next_eps=1e-5)
+    args = (prefix, blocks, up(s.norm), up(s.query), up(s.out_norm), out, aux, ws, up(nn), up(nq),
+            mix[:, :s.H], scal)
+    if packed:
+        Wp = sga.attnres_pack_weights(up(s.W))
+        sga.attnres_oproj_packed_ahead_run(up(s.x), Wp, s.H, *args, **kw)
+    else:
+        sga.attnres_oproj_ahead_run(up(s.x), up(s.W), *args, **kw)
+    assert sga.attnres_workspace_status(ws) == 0
+    torch.cuda.synchronize()
+    res = {k: down(v) for k, v in (("out", out), ("prefix", prefix), ("blocks", blocks),
+                                   ("aux", aux))}
+    m = mix.cpu().numpy()
+    assert np.all(np.isnan(m[:, s.H:])), "wrote into the mixture rows' padding"
+    res["mixture"] = m[:, :s.H].view(np.uint32)
+    res["scal"] = scal.cpu().numpy().view(np.uint32)
+    return res
+
+
+@pytest.mark.parametrize("M,K,H,nb,cap,write,final", [
+    (1, 1024, 7168, 1, 1, -1, 0),    # one token, config 0 shape
+    (8, 4096, 7168, 4, 4, -1, 1),    # config 1 shape, final boundary
+    (13, 1000, 1024, 3, 4, 2, 0),    # ragged K, a scored slot written
+    (40, 1000, 1024, 3, 4, 3, 0),    # split K, a block written after the scored ones
+])
+def test_packed_ahead_equals_row_major_ahead(M, K, H, nb, cap, write, final):
+    """The look-ahead statistics do not involve W: bit-equal to the row-major
+    call's. The step's own outputs equal the plain prepared call's bit for bit
+    and, up to 32 tokens, the row-major look-ahead call's too."""
+    s = synth.decode_step(M, K, nb, H=H, cap=cap, write=write, has_delta=1, seed=700 + M + K)
+    n = synth.decode_step(1, None, 0, H=H, seed=78, layer=1)
+    a = _run_ahead(s, n.norm, n.query, packed=True, final=final)
+    b = _run_ahead(s, n.norm, n.query, packed=False, final=final)
+    for k in ("mixture", "scal"):
+        assert np.array_equal(a[k], b[k]), f"M={M}: look-ahead {k} differs"
+    plain = _run(s, packed=True, final=final)
+    for k in ("out", "prefix", "blocks", "aux"):
+        assert np.array_equal(a[k], plain[k]), f"M={M}: {k} differs from the plain prepared call"
+        if M <= 32:
+            assert np.array_equal(a[k], b[k]), f"M={M}: {k} differs from the row-major call"
