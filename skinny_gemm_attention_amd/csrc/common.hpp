@@ -83,6 +83,7 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 constexpr unsigned kBufferOff = 0xFFFFFFF0u;  // past num_records: reads zeros
 constexpr int kBufferDword3 = 0x00020000;     // raw buffer, 32-bit data format
 constexpr int kCacheNTLoad = 2;               // buffer-load cache policy: non-temporal
+constexpr int kCacheNTStore = 2;              // buffer-store cache policy: non-temporal
 // Streamed-once data (the weight matrix): non-temporal hint.
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));

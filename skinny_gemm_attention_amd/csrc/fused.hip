@@ -108,6 +108,12 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
 
   if (g < G) {
     // ---- GEMM role: rows [row0, row0 + rows) for all M tokens -----------------------
+    // Nothing is outstanding here; the explicit wait tells the compiler so.
+    // Its control flow joins the owner role's exit with this entry, and its
+    // wait bookkeeping then carried the owner's loads into this role: a
+    // vmcnt(0) before a fragment read of the ring (a memory round trip) that
+    // came and went with unrelated owner-side changes.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) only
     // Split K: workgroup g < ng streams the even 4 KB blocks (16 chunks) of
     // the K range of row group g and hands its FP32 partials to workgroup
     // g + ng, which streams the odd blocks, adds the two (even part first)
@@ -374,146 +380,197 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
   for (int k = 0; k < KT; ++k) tok[k] = k < ntok ? o + k * NO : o;
   const __amdgpu_buffer_rsrc_t mbox =
       __builtin_amdgcn_make_buffer_rsrc(f.mailbox, 0, M * a.H * 2, kBufferDword3);
-  u32x4 nbits[KT][NCH];
-  float pc[KT][NCH][4];
-  float ngo[kOne ? NCH : 1][8];  // new*gains of the one token
-  unsigned pending = 0, todo = 0;
-#pragma unroll
-  for (int k = 0; k < KT; ++k)
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      nbits[k][j] = u32x4{0u, 0u, 0u, 0u};
-      pc[k][j][0] = pc[k][j][1] = pc[k][j][2] = 0.0f;
-      pc[k][j][3] = pm2[k][j];
-      if (k < ntok && tid + j * NT < CH) pending |= 1u << (k * NCH + j);
-    }
-#pragma unroll
-  for (int j = 0; j < (kOne ? NCH : 1); ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ngo[j][i] = 0.0f;
-  // a chunk that has arrived: form its partials (stores wait until the end:
-  // a wavefront's loads of the next round would wait for them too)
-  auto absorb = [&](unsigned& bits) {
+  // With two tokens per owner the post phase runs twice, as one copy of its
+  // code: a dry pass right after pre() (the owners' idle time while W
+  // streams), whose reductions run on zeros and whose stores go to empty
+  // buffer ranges (the hardware drops them), then the real pass, which then
+  // runs warm (64 tokens, K = 8192: 30.7 -> 30.3 us). With one token the
+  // owner has no such slack (one token, K = 1024: +1.0 us; eight tokens,
+  // K = 4096: +0.3 us), so it runs the real pass only.
+  constexpr bool kDry = KT > 1;
+  auto post = [&](const bool live) {
+    const unsigned row_bytes = live ? (unsigned)(2 * a.H) : 0u;  // 0: stores dropped
+    u32x4 nbits[KT][NCH];
+    float pc[KT][NCH][4];
+    float ngo[kOne ? NCH : 1][8];  // new*gains of the one token
+    unsigned pending = 0, todo = 0;
 #pragma unroll
     for (int k = 0; k < KT; ++k)
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
-        const unsigned bit = 1u << (k * NCH + j);
-        if (bits & bit) {
-          const int c = tid + j * NT;
-          float nw[8], mx[8];
-          unpack8(nbits[k][j], nw);
-          if (kOne) {
+        nbits[k][j] = u32x4{0u, 0u, 0u, 0u};
+        pc[k][j][0] = pc[k][j][1] = pc[k][j][2] = 0.0f;
+        pc[k][j][3] = pm2[k][j];
+        if (k < ntok && tid + j * NT < CH) pending |= 1u << (k * NCH + j);
+      }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              mx[i] = mix1[kOne ? j : 0][i];
-              ngo[kOne ? j : 0][i] = nw[i] * gg[j][i];
+    for (int j = 0; j < (kOne ? NCH : 1); ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ngo[j][i] = 0.0f;
+    if (!live) {  // every chunk "arrived" as zeros
+      todo = pending;
+      pending = 0;
+    }
+    // a chunk that has arrived: form its partials (stores wait until the end:
+    // a wavefront's loads of the next round would wait for them too)
+    auto absorb = [&](unsigned& bits) {
+#pragma unroll
+      for (int k = 0; k < KT; ++k)
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          const unsigned bit = 1u << (k * NCH + j);
+          if (bits & bit) {
+            const int c = tid + j * NT;
+            float nw[8], mx[8];
+            unpack8(nbits[k][j], nw);
+            if (kOne) {
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                mx[i] = mix1[kOne ? j : 0][i];
+                ngo[kOne ? j : 0][i] = nw[i] * gg[j][i];
+              }
+            } else {
+              load_mix(sm.o.mix[k], c, true, mx);
             }
-          } else {
-            load_mix(sm.o.mix[k], c, true, mx);
+            float q[3];
+            chunk_post_new(nw, w[j], mx, q);
+            pc[k][j][0] = q[0];
+            pc[k][j][1] = q[1];
+            pc[k][j][2] = q[2];
           }
-          float q[3];
-          chunk_post_new(nw, w[j], mx, q);
-          pc[k][j][0] = q[0];
-          pc[k][j][1] = q[1];
-          pc[k][j][2] = q[2];
         }
+      bits = 0;
+    };
+    for (int spin = 0; pending != 0; ++spin) {
+      u32x4 r[KT][NCH];
+#pragma unroll
+      for (int k = 0; k < KT; ++k)
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          const bool p = pending & (1u << (k * NCH + j));
+          const unsigned off = (unsigned)tok[k] * (unsigned)(2 * a.H) + 16u * (unsigned)(tid + j * NT);
+          r[k][j] = __builtin_amdgcn_raw_buffer_load_b128(mbox, p ? off : kBufferOff, 0, kCacheSC1);
+        }
+      absorb(todo);  // the previous round's arrivals, while these loads are in flight
+#pragma unroll
+      for (int k = 0; k < KT; ++k)
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          const unsigned bit = 1u << (k * NCH + j);
+          const u32x4 v = r[k][j];
+          if ((pending & bit) && v.x != kMailboxSentinel && v.y != kMailboxSentinel &&
+              v.z != kMailboxSentinel && v.w != kMailboxSentinel) {
+            pending &= ~bit;
+            todo |= bit;
+            nbits[k][j] = v;
+          }
+        }
+      if (pending == 0) break;
+      if (spin >= kSpinLimit) {  // gave up: flag the workspace (results invalid)
+        __hip_atomic_store(&f.ws->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
       }
-    bits = 0;
-  };
-  for (int spin = 0; pending != 0; ++spin) {
-    u32x4 r[KT][NCH];
+      __builtin_amdgcn_s_sleep(2);
+    }
+    absorb(todo);
+    // re-arm the collected mailbox words for the next call (device scope, like
+    // every mailbox access), one 16-byte store per chunk (two 8-byte stores
+    // were 0.18 us slower per step at 8 tokens); nothing below waits for them
+    const __amdgpu_buffer_rsrc_t rearm =
+        __builtin_amdgcn_make_buffer_rsrc(f.mailbox, 0, live ? M * a.H * 2 : 0, kBufferDword3);
 #pragma unroll
     for (int k = 0; k < KT; ++k)
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const bool p = pending & (1u << (k * NCH + j));
-        const unsigned off = (unsigned)tok[k] * (unsigned)(2 * a.H) + 16u * (unsigned)(tid + j * NT);
-        r[k][j] = __builtin_amdgcn_raw_buffer_load_b128(mbox, p ? off : kBufferOff, 0, kCacheSC1);
-      }
-    absorb(todo);  // the previous round's arrivals, while these loads are in flight
-#pragma unroll
-    for (int k = 0; k < KT; ++k)
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const unsigned bit = 1u << (k * NCH + j);
-        const u32x4 v = r[k][j];
-        if ((pending & bit) && v.x != kMailboxSentinel && v.y != kMailboxSentinel &&
-            v.z != kMailboxSentinel && v.w != kMailboxSentinel) {
-          pending &= ~bit;
-          todo |= bit;
-          nbits[k][j] = v;
-        }
-      }
-    if (pending == 0) break;
-    if (spin >= kSpinLimit) {  // gave up: flag the workspace (results invalid)
-      __hip_atomic_store(&f.ws->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-  absorb(todo);
-  // re-arm the collected mailbox words for the next call (device scope, like
-  // every mailbox access), one 16-byte store per chunk (two 8-byte stores
-  // were 0.18 us slower per step at 8 tokens); nothing below waits for them
-#pragma unroll
-  for (int k = 0; k < KT; ++k)
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = tid + j * NT;
-      if (k < ntok && c < CH) {
-        const u32x4 sent = {kMailboxSentinel, kMailboxSentinel, kMailboxSentinel, kMailboxSentinel};
-        __builtin_amdgcn_raw_buffer_store_b128(sent, mbox, (unsigned)tok[k] * (unsigned)(2 * a.H) + 16u * (unsigned)c, 0, kCacheSC1);
-      }
-    }
-  float pp[4 * KT];
-#pragma unroll
-  for (int k = 0; k < KT; ++k)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float s4 = 0.0f;
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) s4 += pc[k][j][i];  // chunk order, as post_partials
-      pp[4 * k + i] = s4;
-    }
-  wg_sum<4 * KT, NW>(pp, lds_pre);  // lds_pre is free: the last pre() ended with a barrier
-
-#pragma unroll
-  for (int k = 0; k < KT; ++k) {
-    if (k < ntok) {
-      const int t = o + k * NO;
-      float nw[NCH][8], ng[NCH][8], mix[NCH][8], mg[NCH][8];
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int c = tid + j * NT;
-        unpack8(nbits[k][j], nw[j]);
-        if (kOne) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            mix[j][i] = mix1[kOne ? j : 0][i];
-            mg[j][i] = mg1[kOne ? j : 0][i];
-            ng[j][i] = ngo[kOne ? j : 0][i];
-          }
-        } else {
-          load_mix(sm.o.mix[k], c, c < CH, mix[j]);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            ng[j][i] = nw[j][i] * gg[j][i];
-            mg[j][i] = mix[j][i] * gg[j][i];
-          }
+        if (k < ntok && c < CH) {
+          const u32x4 sent = {kMailboxSentinel, kMailboxSentinel, kMailboxSentinel, kMailboxSentinel};
+          __builtin_amdgcn_raw_buffer_store_b128(sent, rearm, (unsigned)tok[k] * (unsigned)(2 * a.H) + 16u * (unsigned)c, 0, kCacheSC1);
         }
       }
-      if (a.write >= 0 && a.write < a.nb) {  // a scored slot: written after pre() read it
+    float pp[4 * KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float s4 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) s4 += pc[k][j][i];  // chunk order, as post_partials
+        pp[4 * k + i] = s4;
+      }
+    wg_sum<4 * KT, NW>(pp, lds_pre);  // lds_pre is free: pre() and the last pass end with a barrier
+
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      if (k < ntok) {
+        const int t = o + k * NO;
+        float nw[NCH][8], ng[NCH][8], mix[NCH][8], mg[NCH][8];
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
           const int c = tid + j * NT;
-          if (c < CH) st16<WT>(a.blocks + t * a.bst_t + a.write * a.bst_b + (size_t)c * 8, nbits[k][j]);
+          unpack8(nbits[k][j], nw[j]);
+          if (kOne) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              mix[j][i] = mix1[kOne ? j : 0][i];
+              mg[j][i] = mg1[kOne ? j : 0][i];
+              ng[j][i] = ngo[kOne ? j : 0][i];
+            }
+          } else {
+            load_mix(sm.o.mix[k], c, c < CH, mix[j]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              ng[j][i] = nw[j][i] * gg[j][i];
+              mg[j][i] = mix[j][i] * gg[j][i];
+            }
+          }
         }
+        if (a.write >= 0 && a.write < a.nb) {  // a scored slot: written after pre() read it
+          uint16_t* row = a.blocks + t * a.bst_t + a.write * a.bst_b;
+          if constexpr (kDry) {
+            const __amdgpu_buffer_rsrc_t brow = __builtin_amdgcn_make_buffer_rsrc(row, 0, row_bytes, kBufferDword3);
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+              const int c = tid + j * NT;
+              __builtin_amdgcn_raw_buffer_store_b128(nbits[k][j], brow, c < CH ? 16u * c : kBufferOff,
+                                                     0, WT ? kCacheSC1 : kCacheNTStore);
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+              const int c = tid + j * NT;
+              if (c < CH) st16<WT>(row + (size_t)c * 8, nbits[k][j]);
+            }
+          }
+        }
+        const float tot[4] = {pp[4 * k], pp[4 * k + 1], pp[4 * k + 2], pp[4 * k + 3]};
+        if constexpr (kDry) {
+          float res[NCH][8];
+          out_values<NT, NCH>(a, out_coefs(a, pre[k], tot), nw, ng, mix, mg, gg, lds_fin, res);
+          const __amdgpu_buffer_rsrc_t orow =
+              __builtin_amdgcn_make_buffer_rsrc(a.out + (size_t)t * a.ld_out, 0, row_bytes, kBufferDword3);
+#pragma unroll
+          for (int j = 0; j < NCH; ++j) {
+            const int c = tid + j * NT;
+            __builtin_amdgcn_raw_buffer_store_b128(pack8(res[j]), orow, c < CH ? 16u * c : kBufferOff,
+                                                   0, kCacheNTStore);
+          }
+        } else {
+          finish_out<NT, NCH, false>(a, t, out_coefs(a, pre[k], tot), nw, ng, mix, mg, gg, lds_fin);
+        }
+        if (a.final_b) lds_barrier();  // lds_fin is reused by the next token
       }
-      const float tot[4] = {pp[4 * k], pp[4 * k + 1], pp[4 * k + 2], pp[4 * k + 3]};
-      finish_out<NT, NCH, false>(a, t, out_coefs(a, pre[k], tot), nw, ng, mix, mg, gg, lds_fin);
-      if (a.final_b) lds_barrier();  // lds_fin is reused by the next token
     }
+  };
+  if constexpr (kDry) {
+    const int passes = 2 + (__builtin_amdgcn_readfirstlane(M) >> 30);  // 2, opaque: one copy
+#pragma clang loop unroll(disable)
+    for (int pass = 0; pass < passes; ++pass) {
+      post(pass + 1 == passes);
+      lds_barrier();  // lds_pre is reused by the next pass
+    }
+  } else {
+    post(true);
   }
 }
 
