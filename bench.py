@@ -57,12 +57,12 @@ FOOTPRINT = 640e6
 # sources differ.
 KERNEL_SOURCES = ("common.hpp", "token.hpp", "gemm.hpp", "launch.hpp", "fused.hip")
 MEASURED_TRAFFIC = {  # (workload, "prepared" | "row-major") -> {"digest", "fetch", "write"}
-    (1, "prepared"): {"digest": "77d051b1ab7da6c2d25c12d8f322d17e7524a8ad1b3ff2a3c798aa9df7aa5842", "fetch": 61038201, "write": 1583616},
-    (1, "row-major"): {"digest": "77d051b1ab7da6c2d25c12d8f322d17e7524a8ad1b3ff2a3c798aa9df7aa5842", "fetch": 61039804, "write": 1583616},
-    (0, "prepared"): {"digest": "77d051b1ab7da6c2d25c12d8f322d17e7524a8ad1b3ff2a3c798aa9df7aa5842", "fetch": 14996643, "write": 197952},
-    (0, "row-major"): {"digest": "77d051b1ab7da6c2d25c12d8f322d17e7524a8ad1b3ff2a3c798aa9df7aa5842", "fetch": 14992718, "write": 197952},
-    (2, "prepared"): {"digest": "77d051b1ab7da6c2d25c12d8f322d17e7524a8ad1b3ff2a3c798aa9df7aa5842", "fetch": 139267779, "write": 9175040},
-    (2, "row-major"): {"digest": "77d051b1ab7da6c2d25c12d8f322d17e7524a8ad1b3ff2a3c798aa9df7aa5842", "fetch": 139130706, "write": 9175040},
+    (1, "prepared"): {"digest": "895b658da3e29ac29c1d8b96a68f56edb405b36ce07ecaa867a19287db16759d", "fetch": 61049699, "write": 1468928},
+    (1, "row-major"): {"digest": "895b658da3e29ac29c1d8b96a68f56edb405b36ce07ecaa867a19287db16759d", "fetch": 61041855, "write": 1468928},
+    (0, "prepared"): {"digest": "895b658da3e29ac29c1d8b96a68f56edb405b36ce07ecaa867a19287db16759d", "fetch": 14983808, "write": 183616},
+    (0, "row-major"): {"digest": "895b658da3e29ac29c1d8b96a68f56edb405b36ce07ecaa867a19287db16759d", "fetch": 14984850, "write": 183616},
+    (2, "prepared"): {"digest": "895b658da3e29ac29c1d8b96a68f56edb405b36ce07ecaa867a19287db16759d", "fetch": 139252490, "write": 9175040},
+    (2, "row-major"): {"digest": "895b658da3e29ac29c1d8b96a68f56edb405b36ce07ecaa867a19287db16759d", "fetch": 139192278, "write": 9175040},
 }
 
 WORKLOADS = {
