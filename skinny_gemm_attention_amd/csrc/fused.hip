@@ -499,6 +499,17 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
         pp[4 * k + i] = s4;
       }
     wg_sum<4 * KT, NW>(pp, lds_pre);  // lds_pre is free: pre() and the last pass end with a barrier
+    // two tokens: both output coefficients first, so their scalar chains
+    // overlap (64 tokens: 0.05-0.1 us per step; with one token the same order
+    // was slower)
+    OutCoefs sc[KT];
+    if constexpr (kDry) {
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        const float tot[4] = {pp[4 * k], pp[4 * k + 1], pp[4 * k + 2], pp[4 * k + 3]};
+        sc[k] = out_coefs(a, pre[k], tot);
+      }
+    }
 
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
@@ -546,7 +557,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
         const float tot[4] = {pp[4 * k], pp[4 * k + 1], pp[4 * k + 2], pp[4 * k + 3]};
         if constexpr (kDry) {
           float res[NCH][8];
-          out_values<NT, NCH>(a, out_coefs(a, pre[k], tot), nw, ng, mix, mg, gg, lds_fin, res);
+          out_values<NT, NCH>(a, sc[k], nw, ng, mix, mg, gg, lds_fin, res);
           const __amdgpu_buffer_rsrc_t orow =
               __builtin_amdgcn_make_buffer_rsrc(a.out + (size_t)t * a.ld_out, 0, row_bytes, kBufferDword3);
 #pragma unroll
