@@ -52,17 +52,6 @@ namespace attnres {
 
 constexpr int kMaxTokensPerOwner = 2;
 
-__device__ __forceinline__ void load_mix(const float* row, int c, bool valid, float (&m)[8]) {
-  if (valid) {
-    const f32x4* pm = reinterpret_cast<const f32x4*>(row + c * 8);
-    const f32x4 m0 = pm[0], m1 = pm[1];
-    m[0] = m0.x; m[1] = m0.y; m[2] = m0.z; m[3] = m0.w;
-    m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m[i] = 0.0f;
-  }
-}
 
 template <bool SPLIT, int RT, int TT, bool PACKED>
 struct FusedCore {
@@ -90,11 +79,8 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
   constexpr int KT = TT <= 2 ? 1 : kMaxTokensPerOwner;
   constexpr int NCH = TokenShape<NT>::NCH;
   constexpr bool kOne = KT == 1;
-  union Smem {
+  struct Smem {
     char ring[C::kLdsBytes];  // GEMM role: chunk ring, then the K partials
-    struct {
-      float mix[kOne ? 1 : KT][kOne ? 1 : kMaxH];  // owner role, several tokens
-    } o;
   };
   __shared__ __attribute__((aligned(16))) Smem sm;
   f32x4* red = reinterpret_cast<f32x4*>(sm.ring);
@@ -314,15 +300,23 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
   token_weights<NT, NCH>(a, w, gg);
   if constexpr (AHEAD) pair_weights<NT, NCH>(f.ah.norm, f.ah.query, a.H, w2);
   BlockStats pre[KT];
-  // one token: its mixture (and mixture*gains) stay in registers; more
-  // tokens park their mixtures in LDS
+  // the mixtures of this thread's chunks stay in registers: with one token,
+  // with mixture*gains beside them; with two, the mixtures alone (before,
+  // parked in LDS: 64 tokens 0.23 us slower, the tail's partials and outputs
+  // waiting for the reads)
   float mix1[kOne ? NCH : 1][8], mg1[kOne ? NCH : 1][8];
+  float mixk[kOne ? 1 : KT][kOne ? 1 : NCH][8];
   float pm2[KT][NCH];  // per-chunk sums of mix^2 (the post partial that needs no new prefix)
 #pragma unroll
   for (int k = 0; k < KT; ++k) {
     pre[k] = BlockStats{0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) pm2[k][j] = 0.0f;
+    for (int j = 0; j < NCH; ++j) {
+      pm2[k][j] = 0.0f;
+      if (!kOne)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mixk[kOne ? 0 : k][kOne ? 0 : j][i] = 0.0f;
+    }
     if (k < ntok) {
       const int t = o + k * NO;
       float mix[NCH][8];
@@ -360,9 +354,8 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
             mg1[kOne ? j : 0][i] = mix[j][i] * gg[j][i];
           }
         } else if (c < CH) {
-          f32x4* pm = reinterpret_cast<f32x4*>(sm.o.mix[k] + c * 8);
-          pm[0] = f32x4{mix[j][0], mix[j][1], mix[j][2], mix[j][3]};
-          pm[1] = f32x4{mix[j][4], mix[j][5], mix[j][6], mix[j][7]};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) mixk[kOne ? 0 : k][kOne ? 0 : j][i] = mix[j][i];
         }
       }
       lds_barrier();  // lds_pre is reused by the next token
@@ -430,7 +423,8 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
                 ngo[kOne ? j : 0][i] = nw[i] * gg[j][i];
               }
             } else {
-              load_mix(sm.o.mix[k], c, true, mx);
+#pragma unroll
+              for (int i = 0; i < 8; ++i) mx[i] = mixk[kOne ? 0 : k][kOne ? 0 : j][i];
             }
             float q[3];
             chunk_post_new(nw, w[j], mx, q);
@@ -528,7 +522,8 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
               ng[j][i] = ngo[kOne ? j : 0][i];
             }
           } else {
-            load_mix(sm.o.mix[k], c, c < CH, mix[j]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) mix[j][i] = mixk[kOne ? 0 : k][kOne ? 0 : j][i];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
               ng[j][i] = nw[j][i] * gg[j][i];
