@@ -9,20 +9,25 @@
 //     columns to bf16 (-0.0 -> +0.0), form new = bf16(prefix + y) (or y), store
 //     new to prefix, aux and, when the written slot is not scored, the block
 //     slot, and post it to the token's mailbox row. They never wait.
-//   * Owner workgroups G + o (o < NO) own tokens o, o + NO, ... (at most four):
-//     they run pre() on each token's saved blocks while the GEMM workgroups
-//     stream W (ClusterAttnRes.state: pre needs nothing the GEMM produces),
-//     then collect each token's new prefix from its mailbox row and run post().
+//   * Owner workgroups G + o (o < NO) own tokens o and o + NO (one token up to
+//     32 tokens, two beyond): they run pre() on each token's saved blocks
+//     while the GEMM workgroups stream W (ClusterAttnRes.state: pre needs
+//     nothing the GEMM produces), then collect each token's new prefix from
+//     its mailbox row and run post().
+// Beyond 32 tokens each 64-row group of W is streamed by two GEMM workgroups
+// taking alternate 4 KB blocks of K; the first hands its FP32 partial
+// products to the second (a higher id) through the same sentinel scheme, and
+// the second forms and posts the new prefix.
 // R (even, at most 32) is chosen so that G + NO fits the compute units (for
 // H = 7168: 239 GEMM workgroups of 30 rows): the owners' saved-block reads then
-// overlap the W stream on units of their own instead of extending it. Owners
-// are the highest workgroup ids and wait only on workgroups that never wait,
-// so the grid drains whatever the residency.
+// overlap the W stream on units of their own instead of extending it. Every
+// wait is on a lower workgroup id (owners are the highest ids), so with
+// workgroups dispatched in id order the grid drains whatever the residency.
 //
 // With look-ahead statistics (fused_ahead_kernel; oproj.prepared page,
 // PreparedOproj.bind_ahead) the owners also form, from the saved blocks they
 // already hold, the pre() state of the next layer's AttnRes (its norm, query
-// and eps) and store it: mixture row and (maximum, exp_sum) per token.
+// and eps) and store it: mixture row and (anchor, weight total) per token.
 //
 // Mailbox hand-off (the sentinel scheme of the pages' Lamport mailboxes,
 // oproj.prepared page and positive_zero on the gemm.ws_gemm page): every
