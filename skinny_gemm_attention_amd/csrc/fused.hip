@@ -681,12 +681,20 @@ hipError_t launch_fused(const FusedParams& p, hipStream_t stream) {
                      : go<4, 4, true>(q, kSplitRows, 2 * ng, NO, stream);
     }
   }
-  // GEMM rows per workgroup: even, at most 32, leaving NO compute units free
+  // GEMM rows per workgroup: even, at most 32, leaving NO compute units free.
+  // On prepared W, 28 or 30 become 32: whole 16-row MFMA tiles and fewer
+  // producers move the same bytes (7168 rows, 8 tokens: 224 workgroups of 32
+  // rows instead of 239 of 30, 13.71 -> 13.64 us; a copy with the same ring
+  // streams W as fast with 224 workgroups as with 239 or 256). Not on
+  // row-major W: workgroups 32 rows apart start 256 KiB apart there, and
+  // their concurrent chunk loads then fall on the same memory channels
+  // (K = 4096: 14.2 -> 18.0 us).
   int room = compute_units() - NO;
   if (room < 1) room = 1;
   int R = (H + room - 1) / room;
   R = (R + 1) & ~1;
   if (R < 2) R = 2;
+  if (R >= 28 && p.wrows > 0) R = 32;
   if (R > 32) R = 32;
   const int G = (H + R - 1) / R;
   if (R > 16) {
