@@ -57,12 +57,12 @@ FOOTPRINT = 640e6
 # sources differ.
 KERNEL_SOURCES = ("common.hpp", "token.hpp", "gemm.hpp", "launch.hpp", "fused.hip")
 MEASURED_TRAFFIC = {  # (workload, "prepared" | "row-major") -> {"digest", "fetch", "write"}
-    (1, "prepared"): {"digest": "1b3c98094986b953a2ae6fd98f251aba22068ca92e14c03e67a3b81c858d03c4", "fetch": 61028260, "write": 1468928},
-    (1, "row-major"): {"digest": "1b3c98094986b953a2ae6fd98f251aba22068ca92e14c03e67a3b81c858d03c4", "fetch": 61020440, "write": 1468928},
-    (0, "prepared"): {"digest": "1b3c98094986b953a2ae6fd98f251aba22068ca92e14c03e67a3b81c858d03c4", "fetch": 14998195, "write": 183616},
-    (0, "row-major"): {"digest": "1b3c98094986b953a2ae6fd98f251aba22068ca92e14c03e67a3b81c858d03c4", "fetch": 14982628, "write": 183616},
-    (2, "prepared"): {"digest": "1b3c98094986b953a2ae6fd98f251aba22068ca92e14c03e67a3b81c858d03c4", "fetch": 139298010, "write": 9175040},
-    (2, "row-major"): {"digest": "1b3c98094986b953a2ae6fd98f251aba22068ca92e14c03e67a3b81c858d03c4", "fetch": 139242338, "write": 9175040},
+    (1, "prepared"): {"digest": "4aa50bc58276497822aa48ed35fc2e2e9cd35d6b36c248a16dfd0ff713f3c710", "fetch": 60878492, "write": 917504},
+    (1, "row-major"): {"digest": "4aa50bc58276497822aa48ed35fc2e2e9cd35d6b36c248a16dfd0ff713f3c710", "fetch": 61035132, "write": 1468928},
+    (0, "prepared"): {"digest": "4aa50bc58276497822aa48ed35fc2e2e9cd35d6b36c248a16dfd0ff713f3c710", "fetch": 14986538, "write": 114688},
+    (0, "row-major"): {"digest": "4aa50bc58276497822aa48ed35fc2e2e9cd35d6b36c248a16dfd0ff713f3c710", "fetch": 14982491, "write": 183616},
+    (2, "prepared"): {"digest": "4aa50bc58276497822aa48ed35fc2e2e9cd35d6b36c248a16dfd0ff713f3c710", "fetch": 139249780, "write": 9175040},
+    (2, "row-major"): {"digest": "4aa50bc58276497822aa48ed35fc2e2e9cd35d6b36c248a16dfd0ff713f3c710", "fetch": 139197662, "write": 9175040},
 }
 
 WORKLOADS = {
