@@ -469,7 +469,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
         __hip_atomic_store(&f.ws->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);  // 1: 0.02-0.04 us faster per step than 2 (0: same as 2, 8: 0.1 us slower)
     }
     absorb(todo);
     // re-arm the collected mailbox words for the next call (device scope, like
