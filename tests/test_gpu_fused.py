@@ -141,6 +141,7 @@ def test_fused_equals_gemm_then_attnres(configs, cfg):
     (40, 2056, 520, 1, 2, 1, 0),    # split K: ragged last row group
     (37, 520, 7168, 0, 1, 0, 1),    # split K, nb = 0 (plain output norm), last owner one token
     (8, 1000, 5008, 2, 3, -1, 1),   # 22-row groups: second row tile partly filled, ragged last group
+    (8, 1000, 7000, 2, 3, 1, 1),    # prepared W: 32-row groups, last one 24 rows; row-major: 30 rows, last 10
 ])
 def test_fused_edges(M, K, H, nb, cap, write, has_delta):
     s = synth.decode_step(M, K, nb, H=H, cap=cap, write=write, has_delta=has_delta, seed=M + K)

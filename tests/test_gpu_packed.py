@@ -105,6 +105,7 @@ def test_packed_equals_row_major_and_oracle(configs, cfg, final):
 @pytest.mark.parametrize("M,K,H,nb,cap,write,has_delta", [
     (13, 1000, 1024, 3, 4, 3, 1),   # ragged K (zero-padded planes), narrower rows
     (8, 1000, 5008, 2, 3, -1, 1),   # 22-row groups: second row tile partly filled, ragged last group
+    (8, 1000, 7000, 2, 3, 1, 1),    # prepared W: 32-row groups, last one 24 rows; row-major: 30 rows, last 10
     (40, 1000, 1024, 3, 4, 1, 1),   # split K, ragged second half
     (48, 264, 7168, 2, 3, -1, 0),   # split K, a second half of one k-step
     (1, 8, 7168, 1, 1, -1, 1),      # K of one piece
