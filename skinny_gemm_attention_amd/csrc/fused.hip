@@ -390,7 +390,7 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
     const unsigned row_bytes = live ? (unsigned)(2 * a.H) : 0u;  // 0: stores dropped
     u32x4 nbits[KT][NCH];
     float pc[KT][NCH][4];
-    float ngo[kOne ? NCH : 1][8];  // new*gains of the one token
+    float ngo[KT][NCH][8];  // new*gains, formed as each chunk arrives
     unsigned pending = 0, todo = 0;
 #pragma unroll
     for (int k = 0; k < KT; ++k)
@@ -402,9 +402,11 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
         if (k < ntok && tid + j * NT < CH) pending |= 1u << (k * NCH + j);
       }
 #pragma unroll
-    for (int j = 0; j < (kOne ? NCH : 1); ++j)
+    for (int k = 0; k < KT; ++k)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ngo[j][i] = 0.0f;
+      for (int j = 0; j < NCH; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ngo[k][j][i] = 0.0f;
     if (!live) {  // every chunk "arrived" as zeros
       todo = pending;
       pending = 0;
@@ -421,15 +423,10 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
             const int c = tid + j * NT;
             float nw[8], mx[8];
             unpack8(nbits[k][j], nw);
-            if (kOne) {
 #pragma unroll
-              for (int i = 0; i < 8; ++i) {
-                mx[i] = mix1[kOne ? j : 0][i];
-                ngo[kOne ? j : 0][i] = nw[i] * gg[j][i];
-              }
-            } else {
-#pragma unroll
-              for (int i = 0; i < 8; ++i) mx[i] = mixk[kOne ? 0 : k][kOne ? 0 : j][i];
+            for (int i = 0; i < 8; ++i) {
+              mx[i] = kOne ? mix1[kOne ? j : 0][i] : mixk[kOne ? 0 : k][kOne ? 0 : j][i];
+              ngo[k][j][i] = nw[i] * gg[j][i];
             }
             float q[3];
             chunk_post_new(nw, w[j], mx, q);
@@ -524,14 +521,14 @@ __device__ __forceinline__ void fused_body(const FusedParams& f, int R, int G, i
             for (int i = 0; i < 8; ++i) {
               mix[j][i] = mix1[kOne ? j : 0][i];
               mg[j][i] = mg1[kOne ? j : 0][i];
-              ng[j][i] = ngo[kOne ? j : 0][i];
+              ng[j][i] = ngo[k][j][i];
             }
           } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) mix[j][i] = mixk[kOne ? 0 : k][kOne ? 0 : j][i];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-              ng[j][i] = nw[j][i] * gg[j][i];
+              ng[j][i] = ngo[k][j][i];
               mg[j][i] = mix[j][i] * gg[j][i];
             }
           }
