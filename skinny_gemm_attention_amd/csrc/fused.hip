@@ -36,7 +36,10 @@
 // that is zero is +0.0), so a word differs from the sentinel exactly when its
 // value has arrived. GEMM workgroups write each pair once with a device-scope
 // (sc1) store; each owner thread polls its own 8-column chunks with
-// device-scope loads, in a fixed chunk order, and re-arms them after reading.
+// device-scope loads, in a fixed chunk order, and re-arms them after reading
+// (never earlier in the call: a word re-armed before its value is posted
+// stays valid in the owner XCD's L2, where the polls can keep reading it; the
+// next call polls after a kernel boundary, whose acquire drops such lines).
 // One memory latency separates a store from its consumer; no counter, fence or
 // cache write-back is involved. A spin limit bounds every wait: a workgroup
 // that gives up records it in the workspace header and carries on to the end
