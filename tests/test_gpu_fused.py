@@ -159,6 +159,18 @@ def test_fused_back_to_back_reuses_workspace():
         check(s, r, final=layer % 2, what=f"layer {layer}")
 
 
+def test_fused_workspace_shared_across_token_counts():
+    """One workspace, sized for the largest call, serves calls with fewer
+    tokens in any order: the split-K partials start after M mailbox rows, so
+    each call's regions fall on words an earlier call used otherwise, and
+    every call must leave all of them armed."""
+    ws = lib().make_workspace(64, 2048, 2, DEV)
+    for i, M in enumerate((64, 8, 1, 37, 33, 16, 64)):
+        s = synth.decode_step(M, 1024, 2, H=2048, write=1, seed=40 + i, layer=i)
+        r = fused(s, final=i % 2, ws=ws)
+        check(s, r, final=i % 2, what=f"call {i}, M={M}")
+
+
 def test_fused_deterministic(configs):
     s = configs[2]
     a, b = fused(s, final=0), fused(s, final=0)
