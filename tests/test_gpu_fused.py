@@ -142,6 +142,8 @@ def test_fused_equals_gemm_then_attnres(configs, cfg):
     (37, 520, 7168, 0, 1, 0, 1),    # split K, nb = 0 (plain output norm), last owner one token
     (8, 1000, 5008, 2, 3, -1, 1),   # 22-row groups: second row tile partly filled, ragged last group
     (8, 1000, 7000, 2, 3, 1, 1),    # prepared W: 32-row groups, last one 24 rows; row-major: 30 rows, last 10
+    (8, 32760, 512, 2, 3, -1, 1),   # long K: 64 chunks per row, ragged last one
+    (40, 32760, 512, 2, 3, 2, 1),   # split K over long rows: eight 4 KB blocks each, ragged last
 ])
 def test_fused_edges(M, K, H, nb, cap, write, has_delta):
     s = synth.decode_step(M, K, nb, H=H, cap=cap, write=write, has_delta=has_delta, seed=M + K)

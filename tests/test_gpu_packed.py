@@ -110,6 +110,8 @@ def test_packed_equals_row_major_and_oracle(configs, cfg, final):
     (48, 264, 7168, 2, 3, -1, 0),   # split K, a second half of one k-step
     (1, 8, 7168, 1, 1, -1, 1),      # K of one piece
     (24, 2056, 520, 2, 3, 2, 1),    # two token tiles, ragged last row group
+    (8, 32760, 512, 2, 3, -1, 1),   # long K: 256 planes, the last zero-padded
+    (40, 32760, 512, 2, 3, 2, 1),   # split K over long rows
 ])
 def test_packed_edges(M, K, H, nb, cap, write, has_delta):
     s = synth.decode_step(M, K, nb, H=H, cap=cap, write=write, has_delta=has_delta,
